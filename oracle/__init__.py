@@ -1,0 +1,31 @@
+"""CPU oracle for the TwoTower denoising step -- TEST INFRASTRUCTURE ONLY.
+
+This package is the plain, slow, obviously correct definition of what the
+HIP library computes, in float64 numpy.  Only the test suite, the smoke check
+and the CPU-baseline leg of the benchmark may import it.  The product path
+(``denoiser_attention_amd``) never imports, calls or links anything here, and
+nothing here imports the product path: the two share no code.  The seeded
+input generator (``denoiser_attention_amd.synth``) is the only thing both
+sides consume, and it holds no arithmetic of the method.
+
+Source of the definitions.  "TwoTower paper" below means *Nemotron-Labs-
+TwoTower: Diffusion Language Modeling with Pretrained Autoregressive Context*
+(Kamalu et al.), as quoted on the bittide.aicompass.dev article page; its
+equations and algorithms are garbled by text extraction, and the readings
+taken are stated next to each function.
+
+* ``block_attn``   -- TwoTower paper §2.1 "Bidirectional Attention", Eq. (1).
+* ``vocab_stats``  -- TwoTower paper §2.2 "Sampling" (confidence of the
+  prediction at each masked position) and Algorithm 2 (the denoiser's
+  distribution p_theta).
+* ``unmask_step``  -- TwoTower paper §2.2 "Sampling" and Algorithm 2
+  (ConfidenceSample), in its fixed-k reading (threshold switched off).
+
+Pins: every function here is checked by the ``-m "not gpu"`` tests against
+brute force in 50-digit arithmetic, closed forms, invariants and library
+routines (tests/test_oracle_*.py).  No function is "parity unpinned".
+"""
+from .block_attn import block_attn, decode_bf16
+from .unmask import vocab_stats, unmask_step, topk_select
+
+__all__ = ["block_attn", "decode_bf16", "vocab_stats", "unmask_step", "topk_select"]
