@@ -1,0 +1,238 @@
+"""Benchmark of one TwoTower denoising step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+the block attention of one denoiser attention layer (tt_block_attn) and the
+confidence-unmask step (tt_unmask_reduce + tt_unmask_commit, which together
+are tt_unmask_step), at the first refinement step of a block (every position
+still masked, the most logits to read).  Inputs are resident in HBM before
+timing starts; several independent input sets are rotated so that the working
+set exceeds the 256 MB Infinity Cache and every step streams from HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+Prints ONE JSON line: block-tokens/s over the timed steps, the roofline of the
+dominant kernel (the vocabulary pass, HBM-bound) measured with HIP events on
+the launch stream, and the CPU oracle timed on the same host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix, published
+METRIC = "denoised block-tokens/s per denoising step; % HBM/MFMA peak"
+DEFAULT_CONFIG = "decode_b8_p2048_l32"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--prefix-len", type=int, default=None)
+    ap.add_argument("--rotate", type=int, default=0, help="input sets rotated (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    """Digest of the vocabulary-pass kernel source; counter-derived traffic is
+    only reported while it matches the digest recorded with the counters."""
+    with open(os.path.join(ROOT, "denoiser_attention_amd", "csrc", "unmask.hip"), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the vocabulary pass from the committed rocprofv3
+    --pmc summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel factor),
+    or None when absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"vocab_reduce_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    d = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or not d or d.group(1) != kernel_source_digest():
+        return None
+    return float(m.group(1))
+
+
+def cpu_baseline(cfg, inp, logits0, mask):
+    """The oracle as it stands, on the host cores, over one full step of the
+    same workload (all heads of the attention call, all masked rows)."""
+    import threadpoolctl
+
+    import oracle
+    blas = [i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
+            if i.get("user_api") == "blas"]
+    threads = max(blas) if blas else 1
+    f = lambda a: oracle.decode_bf16(a) if a.dtype == np.uint16 else a.astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.block_attn(f(inp["q"]), f(inp["k_ctx"]), f(inp["v_ctx"]), inp["prefix_len"],
+                      f(inp["k_blk"]), f(inp["v_blk"]), inp["scale"])
+    t_attn = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.unmask_step(logits0, mask, cfg.k)
+    t_unmask = time.perf_counter() - t0
+    t_step = t_attn + t_unmask
+    B, L = mask.shape
+    return {
+        "value": B * L / t_step, "unit": "block-tokens/s", "cores": threads, "kind": "oracle",
+        "sample": (f"one full step of {cfg.name}: attention over all {cfg.batch}x{cfg.n_q_heads} "
+                   f"(batch, head) pairs in numpy fp64 ({t_attn:.2f} s, BLAS threads={threads}), "
+                   f"unmask of all {int(mask.sum())} masked rows ({t_unmask:.2f} s, one thread)"),
+        "seconds": t_step,
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the "
+              "denoising step shards over sequences with no exchange, so throughput at N GPUs "
+              "is N independent copies of this measurement.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import denoiser_attention_amd as tt
+    from denoiser_attention_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kw = {} if args.prefix_len is None else {"prefix_len": args.prefix_len}
+    cfg = synth.get_config(args.config, **kw)
+    B, L, V = cfg.batch, cfg.block_len, cfg.vocab
+    Hq, Hkv, D, P = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.prefix_len
+    s = 2 if cfg.dtype == "bf16" else 4
+
+    attn_bytes = s * (2 * B * Hq * L * D + 2 * B * Hkv * (P + L) * D)
+    attn_flops = 4 * B * Hq * L * (P + L) * D
+    logits_bytes = B * L * V * 4
+    set_bytes = attn_bytes + logits_bytes
+    R = args.rotate or max(2, int(np.ceil(1.0e9 / set_bytes)))
+    R = min(R, 8)
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    sets = []
+    host0 = None
+    for r in range(R):
+        inp = synth.attn_inputs(cfg, seed=0, step=r)
+        lg = synth.logits(cfg, seed=0, step=r)
+        if r == 0:
+            host0 = (inp, lg)
+        t = {n: up(inp[n]) for n in ("q", "k_ctx", "v_ctx", "k_blk", "v_blk")}
+        t["logits"] = up(lg)
+        sets.append(t)
+        if r:
+            del lg
+    mask = torch.ones((B, L), dtype=torch.uint8, device=dev)
+    mask_out = torch.empty_like(mask)
+    tokens = torch.full((B, L), -1, dtype=torch.int32, device=dev)
+    out = torch.empty((B, Hq, L, D), dtype=sets[0]["q"].dtype, device=dev)
+    dt = sets[0]["q"].dtype
+    attn_ws_n = tt.attn_workspace_bytes(B, P, L, Hq, Hkv, D, dt)
+    attn_ws = torch.empty(max(attn_ws_n, 1), dtype=torch.uint8, device=dev)
+    um_ws = torch.empty(tt.unmask_workspace_bytes(B, L, V), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        t = sets[i % R]
+        if ev is not None:
+            ev[0].record(stream)
+        tt.block_attn(t["q"], t["k_ctx"], t["v_ctx"], P, t["k_blk"], t["v_blk"], cfg.softmax_scale,
+                      out=out, workspace=attn_ws if attn_ws_n else None, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        tt.unmask_reduce(t["logits"], mask, um_ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        tt.unmask_commit(mask, cfg.k, tokens, mask_out, V, um_ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    attn_us = 1e3 * np.mean([e[0].elapsed_time(e[1]) for e in evs])
+    reduce_us = 1e3 * np.mean([e[1].elapsed_time(e[2]) for e in evs])
+
+    n_masked = B * L
+    reduce_bytes = n_masked * V * 4 + B * L          # masked logit rows + mask bytes
+    achieved_gbs = reduce_bytes / (reduce_us * 1e-6) / 1e9
+    attn_tflops = attn_flops / (attn_us * 1e-6) / 1e12
+    attn_t_roof = max(attn_bytes / (HBM_PEAK_GBS * 1e9), attn_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+
+    result = {
+        "metric": METRIC,
+        "value": B * L / (ms_step * 1e-3),
+        "unit": "block-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+fp32" if cfg.dtype == "bf16" else "fp32",
+        "data": "synthetic (seeded N(0,1) Q/K/V, N(0,3) logits with planted peaks; "
+                f"{R} input sets rotated)",
+        "config": {
+            "workload": cfg.name, "batch": B, "prefix_len": P, "block_len": L,
+            "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "vocab": V, "k": cfg.k,
+            "masked_positions": n_masked, "attention_layers_per_step": 1,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "vocab_reduce_kernel (tt_unmask_reduce)",
+            "bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved_gbs / HBM_PEAK_GBS,
+            "traffic": recorded_traffic(cfg.name),
+            "algorithmic_bytes_per_launch": reduce_bytes,
+            "avg_launch_us": reduce_us,
+        },
+        "attention": {
+            "avg_call_us": attn_us, "tflops": attn_tflops,
+            "mfma_frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
+            "roof_us": attn_t_roof * 1e6, "roof_frac": attn_t_roof * 1e6 / attn_us,
+            "algorithmic_bytes": attn_bytes, "flops": attn_flops,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        inp0, lg0 = host0
+        result["cpu_baseline"] = cpu_baseline(cfg, inp0, lg0, np.ones((B, L), np.uint8))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,18 @@
-"""TwoTower denoising-step kernels for AMD MI355X (gfx950)."""
+"""TwoTower denoising-step kernels for AMD MI355X (gfx950).
+
+The compute lives in libtt.so (hand-written HIP kernels behind the C ABI of
+include/tt.h); this package is its thin Python binding plus the seeded
+synthetic-input generator (``synth``).
+
+    block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale)  -> out
+    unmask_step(logits, mask_state, k, tokens)                     -> (tokens, mask_out)
+"""
+from ._binding import (  # noqa: F401
+    LIB_PATH, TTError, attn_workspace_bytes, block_attn, lib, status_string, unmask_commit,
+    unmask_reduce, unmask_step, unmask_workspace_bytes, version,
+)
+
+__all__ = [
+    "LIB_PATH", "TTError", "attn_workspace_bytes", "block_attn", "lib", "status_string",
+    "unmask_commit", "unmask_reduce", "unmask_step", "unmask_workspace_bytes", "version",
+]

@@ -1,0 +1,230 @@
+"""ctypes binding of libtt (include/tt.h).
+
+Argument marshalling only: shape/dtype/device checks, device pointers, the
+current torch stream, and workspace buffers allocated through torch.  Every
+step of the computation runs in the HIP kernels of libtt.so; there is no CPU
+or PyTorch fallback.  If the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtt.so")
+
+TT_OK, TT_EINVAL, TT_EUNSUPPORTED, TT_ENODEV, TT_EHIP = range(5)
+TT_FP32, TT_BF16 = 0, 1
+TT_ATTN_AUTO, TT_ATTN_MFMA, TT_ATTN_SHUFFLE = 0, 1, 2
+_PATHS = {"auto": TT_ATTN_AUTO, "mfma": TT_ATTN_MFMA, "shuffle": TT_ATTN_SHUFFLE}
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+
+class TTError(RuntimeError):
+    """A libtt entry point returned a status other than TT_OK."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+class AttnOpts(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("kv_splits", ctypes.c_int)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGNATURES = {
+    "tt_status_string": (ctypes.c_char_p, [_i]),
+    "tt_version": (ctypes.c_char_p, []),
+    "tt_block_attn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(AttnOpts)]),
+    "tt_block_attn": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _i, _i, _i,
+                           _vp, _sz, _vp]),
+    "tt_block_attn_ex": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _i, _i,
+                              _i, _vp, _sz, _vp, ctypes.POINTER(AttnOpts)]),
+    "tt_unmask_workspace_bytes": (_sz, [_i, _i, _i]),
+    "tt_unmask_step": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "tt_unmask_reduce": (_i, [_vp, _vp, _i, _i, _i, _vp, _sz, _vp]),
+    "tt_unmask_commit": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtt.so (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with `python -m denoiser_attention_amd.build` "
+                    "(hipcc, gfx950).  There is no fallback implementation.")
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGNATURES.items():
+                fn = getattr(handle, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().tt_status_string(status).decode()
+
+
+def version() -> str:
+    return lib().tt_version().decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != TT_OK:
+        raise TTError(status, what)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return TT_FP32
+    if t == torch.bfloat16:
+        return TT_BF16
+    raise TypeError(f"unsupported dtype {t}; expected float32 or bfloat16")
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device, stream) -> int:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _cuda_contig(name: str, t: torch.Tensor, device: torch.device) -> None:
+    _require(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _require(t.is_cuda and t.device == device, f"{name} must be on {device}")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def attn_workspace_bytes(batch, prefix_len, block_len, n_q_heads, n_kv_heads, head_dim,
+                         dtype: torch.dtype, path: str = "auto", kv_splits: int = 0) -> int:
+    opts = AttnOpts(_PATHS[path], kv_splits)
+    n = lib().tt_block_attn_workspace_bytes(batch, prefix_len, block_len, n_q_heads, n_kv_heads,
+                                            head_dim, _dtype_code(dtype), ctypes.byref(opts))
+    if n == SIZE_MAX:
+        raise ValueError("invalid attention shape")
+    return n
+
+
+def block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, *, out=None, out_dtype=None,
+               path: str = "auto", kv_splits: int = 0, workspace=None, stream=None):
+    """Eq. (1) block attention through tt_block_attn_ex; returns ``out``.
+
+    q [B,Hq,L,D]; k_ctx/v_ctx [B,Hkv,Pcap,D] (or None when prefix_len == 0);
+    k_blk/v_blk [B,Hkv,L,D]; all float32 or all bfloat16 on one GPU.
+    """
+    _require(q.dim() == 4, "q must be [B, Hq, L, D]")
+    device = q.device
+    B, Hq, L, D = q.shape
+    for name, t in (("q", q), ("k_blk", k_blk), ("v_blk", v_blk)):
+        _cuda_contig(name, t, device)
+        _require(t.dtype == q.dtype, f"{name} dtype differs from q")
+    _require(k_blk.dim() == 4 and k_blk.shape[0] == B and k_blk.shape[2] == L
+             and k_blk.shape[3] == D, "k_blk must be [B, Hkv, L, D]")
+    _require(v_blk.shape == k_blk.shape, "v_blk must match k_blk")
+    Hkv = k_blk.shape[1]
+    if k_ctx is None or v_ctx is None:
+        _require(k_ctx is None and v_ctx is None and prefix_len == 0,
+                 "k_ctx/v_ctx may be omitted only when prefix_len == 0")
+        Pcap = 0
+    else:
+        for name, t in (("k_ctx", k_ctx), ("v_ctx", v_ctx)):
+            _cuda_contig(name, t, device)
+            _require(t.dtype == q.dtype, f"{name} dtype differs from q")
+        _require(k_ctx.dim() == 4 and k_ctx.shape[0] == B and k_ctx.shape[1] == Hkv
+                 and k_ctx.shape[3] == D, "k_ctx must be [B, Hkv, Pcap, D]")
+        _require(v_ctx.shape == k_ctx.shape, "v_ctx must match k_ctx")
+        Pcap = k_ctx.shape[2]
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, Hq, L, D), dtype=out_dtype, device=device)
+    _cuda_contig("out", out, device)
+    _require(tuple(out.shape) == (B, Hq, L, D), "out must be [B, Hq, L, D]")
+    opts = AttnOpts(_PATHS[path], kv_splits)
+    need = attn_workspace_bytes(B, prefix_len, L, Hq, Hkv, D, q.dtype, path, kv_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().tt_block_attn_ex(
+        _ptr(q), _ptr(k_ctx), _ptr(v_ctx), prefix_len, _ptr(k_blk), _ptr(v_blk), L, Hq, Hkv, D,
+        float(scale), _ptr(out), B, Pcap, _dtype_code(q.dtype), _dtype_code(out.dtype),
+        _ptr(workspace), ws_bytes, _stream(device, stream), ctypes.byref(opts))
+    _check(st, "tt_block_attn")
+    return out
+
+
+def unmask_workspace_bytes(batch, block_len, vocab) -> int:
+    n = lib().tt_unmask_workspace_bytes(batch, block_len, vocab)
+    if n == SIZE_MAX:
+        raise ValueError("invalid unmask shape")
+    return n
+
+
+def _unmask_checks(logits, mask_state, tokens, mask_out, conf_out, pred_out):
+    device = mask_state.device
+    _cuda_contig("mask_state", mask_state, device)
+    _require(mask_state.dtype == torch.uint8 and mask_state.dim() == 2, "mask_state: [B, L] uint8")
+    B, L = mask_state.shape
+    if logits is not None:
+        _cuda_contig("logits", logits, device)
+        _require(logits.dtype == torch.float32 and logits.dim() == 3
+                 and tuple(logits.shape[:2]) == (B, L), "logits: [B, L, V] float32")
+    for name, t, dt in (("tokens", tokens, torch.int32), ("mask_out", mask_out, torch.uint8),
+                        ("conf_out", conf_out, torch.float32), ("pred_out", pred_out, torch.int32)):
+        if t is not None:
+            _cuda_contig(name, t, device)
+            _require(t.dtype == dt and tuple(t.shape) == (B, L), f"{name}: [B, L] {dt}")
+    return device, B, L
+
+
+def unmask_step(logits, mask_state, k, tokens, *, mask_out=None, conf_out=None, pred_out=None,
+                workspace=None, stream=None):
+    """One fixed-k unmask step through tt_unmask_step.  ``tokens`` is updated in
+    place at committed positions; returns (tokens, mask_out)."""
+    device, B, L = _unmask_checks(logits, mask_state, tokens, mask_out, conf_out, pred_out)
+    V = logits.shape[2]
+    if mask_out is None:
+        mask_out = torch.empty_like(mask_state)
+    need = unmask_workspace_bytes(B, L, V)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib().tt_unmask_step(_ptr(logits), _ptr(mask_state), int(k), _ptr(tokens),
+                              _ptr(mask_out), B, L, V, _ptr(conf_out), _ptr(pred_out),
+                              _ptr(workspace), ws_bytes, _stream(device, stream))
+    _check(st, "tt_unmask_step")
+    return tokens, mask_out
+
+
+def unmask_reduce(logits, mask_state, workspace, *, stream=None):
+    """First half of tt_unmask_step (vocabulary pass into ``workspace``)."""
+    device, B, L = _unmask_checks(logits, mask_state, None, None, None, None)
+    st = lib().tt_unmask_reduce(_ptr(logits), _ptr(mask_state), B, L, logits.shape[2],
+                                _ptr(workspace), workspace.numel(), _stream(device, stream))
+    _check(st, "tt_unmask_reduce")
+
+
+def unmask_commit(mask_state, k, tokens, mask_out, vocab, workspace, *, conf_out=None,
+                  pred_out=None, stream=None):
+    """Second half of tt_unmask_step (merge, top-k, commit)."""
+    device, B, L = _unmask_checks(None, mask_state, tokens, mask_out, conf_out, pred_out)
+    st = lib().tt_unmask_commit(_ptr(mask_state), int(k), _ptr(tokens), _ptr(mask_out), B, L,
+                                vocab, _ptr(conf_out), _ptr(pred_out), _ptr(workspace),
+                                workspace.numel(), _stream(device, stream))
+    _check(st, "tt_unmask_commit")

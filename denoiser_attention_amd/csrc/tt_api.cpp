@@ -1,0 +1,325 @@
+// Host side of libtt: argument validation, kernel-family and split planning,
+// workspace layout, and launches on the caller's stream.  The public contract
+// is include/tt.h.  Nothing here allocates device memory.
+#include <climits>
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "tt.h"
+#include "tt_internal.h"
+
+#define TT_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using tt::AttnParams;
+using tt::UnmaskParams;
+
+constexpr size_t kAlign = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+// Workgroups the split heuristic aims for: two resident 256-thread
+// workgroups on each of the 256 CUs for the MFMA kernel; more, smaller
+// one-wave workgroups for the shuffle kernel.
+constexpr long long kMfmaTargetWG = 512;
+constexpr long long kShufTargetWG = 2048;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+
+tt_status device_present() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return TT_ENODEV;
+  }
+  return TT_OK;
+}
+
+struct AttnPlan {
+  int path = TT_ATTN_SHUFFLE;  // resolved family
+  int splits = 1;
+  int tiles_per_split = 1;
+  bool empty = false;          // nothing to compute
+  size_t ws_bytes = 0;
+  size_t lse_offset = 0;
+};
+
+bool mfma_head_dim(int d) { return d == 64 || d == 128; }
+bool shuffle_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
+
+tt_status plan_attn(int B, int P, int L, int Hq, int Hkv, int D, tt_dtype dtype,
+                    const tt_attn_opts* opts, AttnPlan* plan) {
+  if (B < 0 || P < 0 || L < 0 || Hq < 1 || Hkv < 1 || D < 1) return TT_EINVAL;
+  if (Hq % Hkv != 0) return TT_EINVAL;
+  if (dtype != TT_FP32 && dtype != TT_BF16) return TT_EINVAL;
+  const int req = opts ? opts->path : TT_ATTN_AUTO;
+  if (req != TT_ATTN_AUTO && req != TT_ATTN_MFMA && req != TT_ATTN_SHUFFLE) return TT_EINVAL;
+  if (opts && opts->kv_splits < 0) return TT_EINVAL;
+  if ((long long)P + L > INT_MAX / 2) return TT_EUNSUPPORTED;
+  const int G = Hq / Hkv;
+  const long long M = (long long)G * L;
+  if (M > INT_MAX / 2) return TT_EUNSUPPORTED;
+
+  if (req == TT_ATTN_MFMA) {
+    if (dtype != TT_BF16 || !mfma_head_dim(D)) return TT_EUNSUPPORTED;
+    plan->path = TT_ATTN_MFMA;
+  } else if (req == TT_ATTN_SHUFFLE) {
+    if (!shuffle_head_dim(D)) return TT_EUNSUPPORTED;
+    plan->path = TT_ATTN_SHUFFLE;
+  } else {
+    if (dtype == TT_BF16 && M >= 16 && mfma_head_dim(D)) {
+      plan->path = TT_ATTN_MFMA;
+    } else if (shuffle_head_dim(D)) {
+      plan->path = TT_ATTN_SHUFFLE;
+    } else {
+      return TT_EUNSUPPORTED;
+    }
+  }
+  plan->empty = (B == 0 || L == 0);
+  if (plan->empty) {
+    plan->splits = 1;
+    plan->tiles_per_split = 1;
+    plan->ws_bytes = 0;
+    return TT_OK;
+  }
+
+  const long long n_keys = (long long)P + L;
+  long long n_tiles, base, target;
+  if (plan->path == TT_ATTN_MFMA) {
+    n_tiles = cdiv(n_keys, tt::kAttnMfmaBN);
+    base = cdiv(M, tt::kAttnMfmaBM) * B * Hkv;
+    target = kMfmaTargetWG;
+  } else {
+    n_tiles = cdiv(n_keys, tt::kAttnShufBN);
+    base = cdiv(M, tt::kAttnShufRows) * B * Hkv;
+    target = kShufTargetWG;
+  }
+  long long splits;
+  if (opts && opts->kv_splits > 0) {
+    splits = opts->kv_splits < n_tiles ? opts->kv_splits : n_tiles;
+  } else {
+    splits = cdiv(target, base);
+    const long long max_splits = n_tiles / 2 > 1 ? n_tiles / 2 : 1;
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+  }
+  const long long tps = cdiv(n_tiles, splits);
+  splits = cdiv(n_tiles, tps);   // no empty split
+  if (base * splits > INT_MAX) return TT_EUNSUPPORTED;
+  plan->splits = (int)splits;
+  plan->tiles_per_split = (int)tps;
+  if (splits > 1) {
+    const size_t rows = (size_t)B * Hq * L;
+    const size_t o_bytes = align_up((size_t)splits * rows * D * sizeof(float));
+    plan->lse_offset = o_bytes;
+    plan->ws_bytes = o_bytes + align_up((size_t)splits * rows * sizeof(float));
+  } else {
+    plan->ws_bytes = 0;
+  }
+  return TT_OK;
+}
+
+tt_status to_status(hipError_t e) { return e == hipSuccess ? TT_OK : TT_EHIP; }
+
+struct UnmaskPlan {
+  int n_chunks = 0;
+  size_t ws_bytes = 0;
+  bool empty = false;
+};
+
+tt_status plan_unmask(int B, int L, int V, UnmaskPlan* plan) {
+  if (B < 0 || L < 0 || V < 1) return TT_EINVAL;
+  if (L > tt::kUnmaskMaxL) return TT_EUNSUPPORTED;
+  plan->n_chunks = (int)cdiv(V, tt::kVocabChunk);
+  plan->empty = (B == 0 || L == 0);
+  const long long wgs = (long long)B * L * plan->n_chunks;
+  if (wgs > INT_MAX) return TT_EUNSUPPORTED;
+  plan->ws_bytes = plan->empty ? 0 : align_up((size_t)wgs * sizeof(tt::VocabPartial));
+  return TT_OK;
+}
+
+}  // namespace
+
+TT_EXPORT const char* tt_status_string(tt_status s) {
+  switch (s) {
+    case TT_OK: return "TT_OK";
+    case TT_EINVAL: return "TT_EINVAL: invalid argument";
+    case TT_EUNSUPPORTED: return "TT_EUNSUPPORTED: not covered by the compiled kernels";
+    case TT_ENODEV: return "TT_ENODEV: no HIP device visible";
+    case TT_EHIP: return "TT_EHIP: HIP runtime or launch failure";
+  }
+  return "unknown tt_status";
+}
+
+TT_EXPORT const char* tt_version(void) { return "0.1.0"; }
+
+TT_EXPORT size_t tt_block_attn_workspace_bytes(int batch, int prefix_len, int block_len,
+                                               int n_q_heads, int n_kv_heads, int head_dim,
+                                               tt_dtype dtype, const tt_attn_opts* opts) {
+  AttnPlan plan;
+  if (plan_attn(batch, prefix_len, block_len, n_q_heads, n_kv_heads, head_dim, dtype, opts,
+                &plan) != TT_OK)
+    return SIZE_MAX;
+  return plan.ws_bytes;
+}
+
+TT_EXPORT tt_status tt_block_attn_ex(const void* q, const void* k_ctx, const void* v_ctx,
+                                     int prefix_len, const void* k_blk, const void* v_blk,
+                                     int block_len, int n_q_heads, int n_kv_heads, int head_dim,
+                                     float scale, void* out, int batch, int prefix_cap,
+                                     tt_dtype dtype, tt_dtype out_dtype, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream,
+                                     const tt_attn_opts* opts) {
+  AttnPlan plan;
+  tt_status st = plan_attn(batch, prefix_len, block_len, n_q_heads, n_kv_heads, head_dim, dtype,
+                           opts, &plan);
+  if (st != TT_OK) return st;
+  if (prefix_cap < prefix_len) return TT_EINVAL;
+  if (!std::isfinite(scale)) return TT_EINVAL;
+  if (out_dtype != TT_FP32 && out_dtype != TT_BF16) return TT_EINVAL;
+  if (dtype == TT_FP32 && out_dtype != TT_FP32) return TT_EINVAL;
+  if (plan.empty) return TT_OK;
+  if (!q || !k_blk || !v_blk || !out) return TT_EINVAL;
+  if (prefix_cap > 0 && (!k_ctx || !v_ctx)) return TT_EINVAL;
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return TT_EINVAL;
+  st = device_present();
+  if (st != TT_OK) return st;
+
+  AttnParams p{};
+  p.q = q;
+  p.k_ctx = k_ctx;
+  p.v_ctx = v_ctx;
+  p.k_blk = k_blk;
+  p.v_blk = v_blk;
+  p.out = out;
+  p.B = batch;
+  p.Hq = n_q_heads;
+  p.Hkv = n_kv_heads;
+  p.G = n_q_heads / n_kv_heads;
+  p.L = block_len;
+  p.P = prefix_len;
+  p.Pcap = prefix_cap;
+  p.D = head_dim;
+  p.M = p.G * block_len;
+  p.n_keys = prefix_len + block_len;
+  p.splits = plan.splits;
+  p.tiles_per_split = plan.tiles_per_split;
+  p.out_bf16 = out_dtype == TT_BF16 ? 1 : 0;
+  p.scale_log2 = scale * kLog2e;
+  if (plan.splits > 1) {
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.lse_offset);
+  }
+
+  (void)hipGetLastError();  // clear any stale error so it is not reported as ours
+  hipError_t e = plan.path == TT_ATTN_MFMA ? tt::launch_attn_mfma(p, stream)
+                                           : tt::launch_attn_shuffle(p, dtype == TT_BF16, stream);
+  if (e != hipSuccess) return TT_EHIP;
+  if (plan.splits > 1) {
+    e = tt::launch_attn_merge(p, stream);
+    if (e != hipSuccess) return TT_EHIP;
+  }
+  return TT_OK;
+}
+
+TT_EXPORT tt_status tt_block_attn(const void* q, const void* k_ctx, const void* v_ctx,
+                                  int prefix_len, const void* k_blk, const void* v_blk,
+                                  int block_len, int n_q_heads, int n_kv_heads, int head_dim,
+                                  float scale, void* out, int batch, int prefix_cap,
+                                  tt_dtype dtype, tt_dtype out_dtype, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return tt_block_attn_ex(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, block_len, n_q_heads,
+                          n_kv_heads, head_dim, scale, out, batch, prefix_cap, dtype, out_dtype,
+                          workspace, workspace_bytes, stream, nullptr);
+}
+
+TT_EXPORT size_t tt_unmask_workspace_bytes(int batch, int block_len, int vocab) {
+  UnmaskPlan plan;
+  if (plan_unmask(batch, block_len, vocab, &plan) != TT_OK) return SIZE_MAX;
+  return plan.ws_bytes;
+}
+
+namespace {
+
+tt_status unmask_prepare(const float* logits, const uint8_t* mask_state, int batch,
+                         int block_len, int vocab, const void* workspace,
+                         size_t workspace_bytes, UnmaskPlan* plan, UnmaskParams* p) {
+  tt_status st = plan_unmask(batch, block_len, vocab, plan);
+  if (st != TT_OK) return st;
+  if (plan->empty) return TT_OK;
+  if (!mask_state) return TT_EINVAL;
+  if (!workspace || workspace_bytes < plan->ws_bytes) return TT_EINVAL;
+  p->logits = logits;
+  p->mask_state = mask_state;
+  p->partials = static_cast<tt::VocabPartial*>(const_cast<void*>(workspace));
+  p->B = batch;
+  p->L = block_len;
+  p->V = vocab;
+  p->n_chunks = plan->n_chunks;
+  return TT_OK;
+}
+
+}  // namespace
+
+TT_EXPORT tt_status tt_unmask_reduce(const float* logits, const uint8_t* mask_state, int batch,
+                                     int block_len, int vocab, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  UnmaskPlan plan;
+  UnmaskParams p{};
+  tt_status st = unmask_prepare(logits, mask_state, batch, block_len, vocab, workspace,
+                                workspace_bytes, &plan, &p);
+  if (st != TT_OK || plan.empty) return st;
+  if (!logits) return TT_EINVAL;
+  st = device_present();
+  if (st != TT_OK) return st;
+  (void)hipGetLastError();
+  return to_status(tt::launch_vocab_reduce(p, stream));
+}
+
+TT_EXPORT tt_status tt_unmask_commit(const uint8_t* mask_state, int k, int32_t* tokens_out,
+                                     uint8_t* mask_out, int batch, int block_len, int vocab,
+                                     float* conf_out, int32_t* pred_out, const void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  if (k < 0) return TT_EINVAL;
+  UnmaskPlan plan;
+  UnmaskParams p{};
+  tt_status st = unmask_prepare(nullptr, mask_state, batch, block_len, vocab, workspace,
+                                workspace_bytes, &plan, &p);
+  if (st != TT_OK || plan.empty) return st;
+  if (!tokens_out || !mask_out) return TT_EINVAL;
+  st = device_present();
+  if (st != TT_OK) return st;
+  p.k = k;
+  p.tokens_out = tokens_out;
+  p.mask_out = mask_out;
+  p.conf_out = conf_out;
+  p.pred_out = pred_out;
+  (void)hipGetLastError();
+  return to_status(tt::launch_topk_commit(p, stream));
+}
+
+TT_EXPORT tt_status tt_unmask_step(const float* logits, const uint8_t* mask_state, int k,
+                                   int32_t* tokens_out, uint8_t* mask_out, int batch,
+                                   int block_len, int vocab, float* conf_out, int32_t* pred_out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (k < 0) return TT_EINVAL;
+  UnmaskPlan plan;
+  UnmaskParams p{};
+  tt_status st = unmask_prepare(logits, mask_state, batch, block_len, vocab, workspace,
+                                workspace_bytes, &plan, &p);
+  if (st != TT_OK || plan.empty) return st;
+  if (!logits || !tokens_out || !mask_out) return TT_EINVAL;
+  st = device_present();
+  if (st != TT_OK) return st;
+  p.k = k;
+  p.tokens_out = tokens_out;
+  p.mask_out = mask_out;
+  p.conf_out = conf_out;
+  p.pred_out = pred_out;
+  (void)hipGetLastError();
+  hipError_t e = tt::launch_vocab_reduce(p, stream);
+  if (e != hipSuccess) return TT_EHIP;
+  return to_status(tt::launch_topk_commit(p, stream));
+}

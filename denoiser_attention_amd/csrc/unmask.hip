@@ -1,0 +1,215 @@
+// Confidence unmasking: fused vocabulary reduction and per-sequence top-k.
+//
+// Operation: TwoTower paper §2.2 "Sampling" and Algorithm 2 (ConfidenceSample),
+// fixed-k form.  For every still-masked position the denoiser's prediction is
+// the argmax of its logit row and its confidence is the largest softmax
+// probability, 1 / sum_v exp(x_v - max); the k most confident masked positions
+// of each sequence are committed (ties: lower position first), the rest stay
+// masked.  Logit rows of positions that are not masked are never read.
+//
+// vocab_reduce_kernel -- the HBM-bound pass.  A workgroup reduces one 8192-logit
+//   (32 KB) chunk of one masked row: every thread issues all of its 128-bit
+//   loads up front (8 x 16 B), takes the max / lowest-id argmax over its 32
+//   values on the raw fp32 logits, then its sum of exp2((x - max) * log2 e);
+//   the (max, argmax, sum) triples are merged across the wave with xor
+//   shuffles and across the 4 waves through LDS, ties going to the lower id at
+//   every stage.  Chunks of unmasked rows exit at once.
+// topk_commit_kernel -- one workgroup per sequence: merges the chunk triples of
+//   each masked position in chunk order, forms the confidence, ranks every
+//   masked position by counting the masked positions ahead of it in the order
+//   (confidence descending, position ascending) and commits rank < k.
+#include <climits>
+
+#include "tt_internal.h"
+
+namespace tt {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kVecPerThread = kVocabChunk / (kThreads * 4);      // 8 float4 loads
+constexpr int kScalarPerThread = kVocabChunk / kThreads;         // 32 scalar loads
+static_assert(kVocabChunk % (kThreads * 4) == 0, "chunk must be a multiple of 1024");
+
+struct Triple {
+  float m;
+  int arg;
+  float s;
+};
+
+// Merge two (max, lowest argmax, sum of exp(x - max)) triples.  An empty
+// triple is (-inf, INT_MAX, 0).
+__device__ __forceinline__ Triple combine(Triple a, Triple b) {
+  Triple r;
+  r.m = fmaxf(a.m, b.m);
+  const float sa = a.m == -INFINITY ? 0.0f : a.s * __builtin_amdgcn_exp2f((a.m - r.m) * kLog2e);
+  const float sb = b.m == -INFINITY ? 0.0f : b.s * __builtin_amdgcn_exp2f((b.m - r.m) * kLog2e);
+  r.s = sa + sb;
+  r.arg = a.m > b.m ? a.arg : (b.m > a.m ? b.arg : min(a.arg, b.arg));
+  return r;
+}
+
+__device__ __forceinline__ Triple shfl_xor_triple(Triple t, int mask) {
+  Triple o;
+  o.m = __shfl_xor(t.m, mask);
+  o.arg = __shfl_xor(t.arg, mask);
+  o.s = __shfl_xor(t.s, mask);
+  return o;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void vocab_reduce_kernel(UnmaskParams p) {
+  const size_t gid = blockIdx.x;
+  const size_t row = gid / (size_t)p.n_chunks;
+  const int chunk = (int)(gid % (size_t)p.n_chunks);
+  if (p.mask_state[row] == 0) return;
+
+  const int tid = threadIdx.x;
+  const int V = p.V;
+  const int c0 = chunk * kVocabChunk;
+  const int c1 = min(V, c0 + kVocabChunk);
+  const float* x = p.logits + row * (size_t)V;
+
+  Triple t{-INFINITY, INT_MAX, 0.0f};
+  if (VEC) {
+    // V % 4 == 0 and 16-byte aligned rows: ids c0 + i*1024 + 4*tid + {0..3}.
+    f32x4 v[kVecPerThread];
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+      const int idx = c0 + i * (kThreads * 4) + 4 * tid;
+      v[i] = idx < c1 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x + idx))
+                      : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+    // Values are visited in increasing id order; strict '>' keeps the lowest id.
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+      const int idx = c0 + i * (kThreads * 4) + 4 * tid;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (v[i][e] > t.m) { t.m = v[i][e]; t.arg = idx + e; }
+      }
+    }
+    if (t.m != -INFINITY) {
+      const float mb = t.m * kLog2e;
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kVecPerThread; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s += __builtin_amdgcn_exp2f(fmaf(v[i][e], kLog2e, -mb));
+      t.s = s;
+    }
+  } else {
+    float v[kScalarPerThread];
+#pragma unroll
+    for (int i = 0; i < kScalarPerThread; ++i) {
+      const int idx = c0 + i * kThreads + tid;
+      v[i] = idx < c1 ? x[idx] : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < kScalarPerThread; ++i) {
+      if (v[i] > t.m) { t.m = v[i]; t.arg = c0 + i * kThreads + tid; }
+    }
+    if (t.m != -INFINITY) {
+      const float mb = t.m * kLog2e;
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kScalarPerThread; ++i) s += __builtin_amdgcn_exp2f(fmaf(v[i], kLog2e, -mb));
+      t.s = s;
+    }
+  }
+
+#pragma unroll
+  for (int mask = 32; mask >= 1; mask >>= 1) t = combine(t, shfl_xor_triple(t, mask));
+
+  __shared__ Triple s_t[kThreads / 64];
+  const int lane = tid & 63, wave = tid >> 6;
+  if (lane == 0) s_t[wave] = t;
+  __syncthreads();
+  if (tid == 0) {
+    Triple r = s_t[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) r = combine(r, s_t[w]);
+    VocabPartial out;
+    out.m = r.m;
+    out.arg = r.arg;
+    out.s = r.s;
+    out.pad = 0;
+    p.partials[row * (size_t)p.n_chunks + chunk] = out;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void topk_commit_kernel(UnmaskParams p) {
+  __shared__ float s_conf[kUnmaskMaxL];
+  __shared__ int s_pred[kUnmaskMaxL];
+  __shared__ unsigned char s_mask[kUnmaskMaxL];
+
+  const int b = blockIdx.x;
+  const int L = p.L;
+  const int tid = threadIdx.x;
+  const size_t row0 = (size_t)b * L;
+
+  // Every mask flag of the sequence is read before any is written, so
+  // mask_out may alias mask_state.
+  for (int l = tid; l < L; l += kThreads) {
+    const size_t row = row0 + l;
+    const bool masked = p.mask_state[row] != 0;
+    float conf = -1.0f;
+    int pred = -1;
+    if (masked) {
+      const VocabPartial* pp = p.partials + row * (size_t)p.n_chunks;
+      Triple t{-INFINITY, INT_MAX, 0.0f};
+      for (int c = 0; c < p.n_chunks; ++c) {
+        const VocabPartial q = pp[c];
+        t = combine(t, Triple{q.m, q.arg, q.s});
+      }
+      conf = 1.0f / t.s;
+      pred = t.arg;
+    }
+    s_conf[l] = conf;
+    s_pred[l] = pred;
+    s_mask[l] = masked ? 1 : 0;
+  }
+  __syncthreads();
+
+  for (int l = tid; l < L; l += kThreads) {
+    const size_t row = row0 + l;
+    bool commit = false;
+    if (s_mask[l] && p.k > 0) {
+      const float c = s_conf[l];
+      int ahead = 0;
+      for (int j = 0; j < L && ahead < p.k; ++j)
+        ahead += (s_mask[j] && (s_conf[j] > c || (s_conf[j] == c && j < l))) ? 1 : 0;
+      commit = ahead < p.k;
+    }
+    if (commit) p.tokens_out[row] = s_pred[l];
+    p.mask_out[row] = (s_mask[l] && !commit) ? 1 : 0;
+    if (p.conf_out) p.conf_out[row] = s_conf[l];
+    if (p.pred_out) p.pred_out[row] = s_pred[l];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_vocab_reduce(const UnmaskParams& p, hipStream_t stream) {
+  const long long n = (long long)p.B * p.L * p.n_chunks;
+  if (n <= 0 || n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const bool vec = (p.V % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.logits) & 15) == 0);
+  if (vec) {
+    hipLaunchKernelGGL(vocab_reduce_kernel<true>, dim3((unsigned)n), dim3(kThreads), 0, stream,
+                       p);
+  } else {
+    hipLaunchKernelGGL(vocab_reduce_kernel<false>, dim3((unsigned)n), dim3(kThreads), 0, stream,
+                       p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_commit(const UnmaskParams& p, hipStream_t stream) {
+  if (p.B <= 0 || p.L > kUnmaskMaxL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(topk_commit_kernel, dim3((unsigned)p.B), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace tt

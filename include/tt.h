@@ -1,0 +1,178 @@
+/*
+ * tt.h -- C ABI of libtt, the TwoTower denoising-step kernels for AMD MI355X (gfx950).
+ *
+ * One denoising step of the denoiser tower over a block of masked tokens has two
+ * GPU operations, both defined by the TwoTower paper ("Nemotron-Labs-TwoTower:
+ * Diffusion Language Modeling with Pretrained Autoregressive Context", quoted on
+ * the bittide.aicompass.dev article page):
+ *
+ *   tt_block_attn   -- Eq. (1) of §2.1 "Bidirectional Attention": the block's
+ *                      queries attend, under one softmax, to the context tower's
+ *                      layer-aligned KV cache of the clean prefix and, with no
+ *                      causal mask, to every position of their own block.
+ *   tt_unmask_step  -- §2.2 "Sampling" / Algorithm 2 (ConfidenceSample): predict
+ *                      every still-masked position, commit the most confident ones.
+ *                      Implemented in its fixed-k form (k positions per sequence
+ *                      and step, the sampler's deadline floor with the confidence
+ *                      threshold switched off).
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays on the
+ *     current HIP device.  The caller owns every buffer; the library never
+ *     allocates or frees memory and keeps no state between calls.
+ *   - Calls only ENQUEUE work on `stream` (0 = the null stream) and return at
+ *     once.  Results are valid after the caller synchronises the stream.
+ *   - Arguments are validated on the host before anything is enqueued; a bad
+ *     argument returns TT_EINVAL and enqueues nothing.  A combination the
+ *     compiled kernels do not cover returns TT_EUNSUPPORTED.  No visible HIP
+ *     device returns TT_ENODEV.  A failed launch returns TT_EHIP.  Faults inside
+ *     a kernel surface at the caller's stream synchronisation.
+ *   - Workspaces are caller-provided device memory of at least the size the
+ *     matching *_workspace_bytes query returns (NULL is allowed when it returns
+ *     0).  Two calls that run concurrently must not share a workspace.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef TT_H_
+#define TT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TT_OK = 0,
+  TT_EINVAL = 1,        /* invalid argument (null pointer, bad size, short workspace) */
+  TT_EUNSUPPORTED = 2,  /* valid, but not covered by the compiled kernels */
+  TT_ENODEV = 3,        /* no HIP device visible */
+  TT_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+} tt_status;
+
+typedef enum { TT_FP32 = 0, TT_BF16 = 1 } tt_dtype;
+
+/* Attention kernel family.  AUTO picks MFMA for bf16 inputs with at least 16
+ * packed query rows per KV head (n_q_heads / n_kv_heads * block_len >= 16) and a
+ * head_dim of 64 or 128, and the wavefront-shuffle kernel otherwise. */
+typedef enum { TT_ATTN_AUTO = 0, TT_ATTN_MFMA = 1, TT_ATTN_SHUFFLE = 2 } tt_attn_path;
+
+/* Optional tuning knobs of tt_block_attn_ex.  kv_splits = 0 lets the library
+ * choose how many workgroups share one query tile's key range; a positive value
+ * forces that many (clamped so that no split is empty). */
+typedef struct {
+  int path;       /* tt_attn_path */
+  int kv_splits;  /* 0 = auto */
+} tt_attn_opts;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* tt_status_string(tt_status status);
+
+/* Library version, e.g. "0.1.0" (static storage). */
+const char* tt_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Block attention: TwoTower paper §2.1, Eq. (1).                            */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of workspace tt_block_attn / tt_block_attn_ex need for this shape and
+ * these options (opts may be NULL = defaults).  Returns 0 when no workspace is
+ * needed, and SIZE_MAX when the arguments are invalid. */
+size_t tt_block_attn_workspace_bytes(int batch, int prefix_len, int block_len, int n_q_heads,
+                                     int n_kv_heads, int head_dim, tt_dtype dtype,
+                                     const tt_attn_opts* opts);
+
+/* out = softmax(scale * Q Kᵀ) V over the key sequence [cache rows 0..P-1 ; block
+ * rows 0..L-1], for every batch entry b and query head h, where query head h
+ * reads KV head h / (n_q_heads / n_kv_heads).  Every block query sees every
+ * prefix row and every block row (bidirectional inside the block); cache rows
+ * P..prefix_cap-1 are never read.
+ *
+ *   q      [batch, n_q_heads, block_len, head_dim]          dtype
+ *   k_ctx  [batch, n_kv_heads, prefix_cap, head_dim]        dtype  context-tower layer-i K
+ *   v_ctx  [batch, n_kv_heads, prefix_cap, head_dim]        dtype  context-tower layer-i V
+ *          (both may be NULL when prefix_cap == 0)
+ *   prefix_len  P >= 0 valid cache rows (0 = plain bidirectional block attention)
+ *   k_blk  [batch, n_kv_heads, block_len, head_dim]         dtype  denoiser's own layer-i K
+ *   v_blk  [batch, n_kv_heads, block_len, head_dim]         dtype  denoiser's own layer-i V
+ *   block_len   L >= 0 (L == 0 or batch == 0: nothing to do, TT_OK)
+ *   n_q_heads, n_kv_heads  >= 1, n_q_heads a multiple of n_kv_heads
+ *   head_dim    D: 64, 128 or 256 (the MFMA kernel covers 64 and 128)
+ *   scale       finite multiplier of q.k (typically 1/sqrt(D))
+ *   out    [batch, n_q_heads, block_len, head_dim]          out_dtype; must not
+ *          alias any input
+ *   batch       B >= 0
+ *   prefix_cap  allocated cache rows per (b, kv head), >= prefix_len
+ *   dtype       TT_FP32 or TT_BF16 for q/k/v (fp32 accumulation either way)
+ *   out_dtype   dtype, or TT_FP32 for bf16 inputs
+ * Inputs are read only.  The call is deterministic: the same inputs give the
+ * same output bits. */
+tt_status tt_block_attn(const void* q, const void* k_ctx, const void* v_ctx, int prefix_len,
+                        const void* k_blk, const void* v_blk, int block_len, int n_q_heads,
+                        int n_kv_heads, int head_dim, float scale, void* out, int batch,
+                        int prefix_cap, tt_dtype dtype, tt_dtype out_dtype, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* tt_block_attn with explicit kernel-family / split options (opts may be NULL). */
+tt_status tt_block_attn_ex(const void* q, const void* k_ctx, const void* v_ctx, int prefix_len,
+                           const void* k_blk, const void* v_blk, int block_len, int n_q_heads,
+                           int n_kv_heads, int head_dim, float scale, void* out, int batch,
+                           int prefix_cap, tt_dtype dtype, tt_dtype out_dtype, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream, const tt_attn_opts* opts);
+
+/* ------------------------------------------------------------------------ */
+/* Confidence unmask: TwoTower paper §2.2 "Sampling", Algorithm 2.           */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of workspace tt_unmask_step needs (SIZE_MAX for invalid sizes). */
+size_t tt_unmask_workspace_bytes(int batch, int block_len, int vocab);
+
+/* One fixed-k confidence-unmasking step over `batch` blocks of `block_len`
+ * positions.  For every position with mask_state != 0 (still [MASK]):
+ *   pred = argmax_v logits[b,l,v]           (lowest id among equal maxima)
+ *   conf = 1 / sum_v exp(logits[b,l,v] - max_v logits[b,l,v])
+ *        = the largest probability of softmax(logits[b,l,:]).
+ * Then per sequence b, the min(k, n_masked(b)) masked positions first in the
+ * order (conf descending, position ascending) are committed:
+ *   tokens_out[b,l] = pred,  mask_out[b,l] = 0.
+ * Every other position keeps its token (tokens_out is not written there) and
+ * gets mask_out[b,l] = (mask_state[b,l] != 0).  Logit rows of positions that
+ * are not masked are never read.
+ *
+ *   logits      [batch, block_len, vocab]  fp32, finite (NaN/Inf: undefined result)
+ *   mask_state  [batch, block_len]  uint8, nonzero = still [MASK]
+ *   k           >= 0 positions to commit per sequence (0 = no-op)
+ *   tokens_out  [batch, block_len]  int32, in/out
+ *   mask_out    [batch, block_len]  uint8, may alias mask_state
+ *   batch, block_len >= 0 (0: nothing to do), block_len <= 1024; vocab >= 1
+ *   conf_out    optional [batch, block_len] fp32: conf at masked positions,
+ *               -1 elsewhere (NULL = not written)
+ *   pred_out    optional [batch, block_len] int32: pred at masked positions,
+ *               -1 elsewhere (NULL = not written)
+ * The call is deterministic. */
+tt_status tt_unmask_step(const float* logits, const uint8_t* mask_state, int k,
+                         int32_t* tokens_out, uint8_t* mask_out, int batch, int block_len,
+                         int vocab, float* conf_out, int32_t* pred_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* The two halves of tt_unmask_step, for callers that schedule them apart (for
+ * instance to time the vocabulary pass alone).  tt_unmask_reduce writes the
+ * per-chunk (max, argmax, sum of exponentials) partials of every masked row into
+ * the workspace; tt_unmask_commit merges them, selects and commits.  Calling
+ * reduce then commit on one stream with the same workspace, mask_state, batch,
+ * block_len and vocab is exactly tt_unmask_step. */
+tt_status tt_unmask_reduce(const float* logits, const uint8_t* mask_state, int batch,
+                           int block_len, int vocab, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+tt_status tt_unmask_commit(const uint8_t* mask_state, int k, int32_t* tokens_out,
+                           uint8_t* mask_out, int batch, int block_len, int vocab,
+                           float* conf_out, int32_t* pred_out, const void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* TT_H_ */

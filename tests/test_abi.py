@@ -1,0 +1,143 @@
+"""The C ABI on the host: the library loads, exports every entry point the
+header declares, and rejects invalid arguments before touching HIP.  None of
+these tests launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import denoiser_attention_amd as tt
+from denoiser_attention_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tt.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
+                                reason="libtt.so not built (python -m denoiser_attention_amd.build)")
+
+FAKE = 0x1000   # never dereferenced: every call below fails validation first
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tt_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert "tt_block_attn" in names and "tt_unmask_step" in names
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    exported = os.popen(f"nm -D --defined-only {B.LIB_PATH}").read()
+    ours = sorted(set(re.findall(r"\bT (tt_\w+)", exported)))
+    assert ours == names, "library exports must equal the header's declarations"
+
+
+def test_status_strings_and_version():
+    assert tt.status_string(0) == "TT_OK"
+    assert "EINVAL" in tt.status_string(1)
+    assert "unknown" in tt.status_string(99)
+    assert tt.version() == "0.1.0"
+
+
+def attn_call(**kw):
+    a = dict(q=FAKE, k_ctx=FAKE, v_ctx=FAKE, prefix_len=64, k_blk=FAKE, v_blk=FAKE, block_len=16,
+             hq=4, hkv=1, d=64, scale=0.125, out=FAKE, batch=1, pcap=64, dtype=B.TT_FP32,
+             odt=B.TT_FP32, ws=None, wsb=0, stream=None, opts=None)
+    a.update(kw)
+    opts = None if a["opts"] is None else ctypes.byref(B.AttnOpts(*a["opts"]))
+    return tt.lib().tt_block_attn_ex(a["q"], a["k_ctx"], a["v_ctx"], a["prefix_len"], a["k_blk"],
+                                     a["v_blk"], a["block_len"], a["hq"], a["hkv"], a["d"],
+                                     a["scale"], a["out"], a["batch"], a["pcap"], a["dtype"],
+                                     a["odt"], a["ws"], a["wsb"], a["stream"], opts)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(k_blk=None), dict(v_blk=None), dict(out=None),
+    dict(k_ctx=None), dict(v_ctx=None),
+    dict(batch=-1), dict(block_len=-1), dict(prefix_len=-1), dict(hq=0), dict(hkv=0),
+    dict(hq=6, hkv=4), dict(pcap=10), dict(scale=float("inf")), dict(scale=float("nan")),
+    dict(dtype=7), dict(odt=7), dict(dtype=B.TT_FP32, odt=B.TT_BF16),
+    dict(opts=(9, 0)), dict(opts=(0, -1)),
+    # bf16 with a split that needs a workspace, none given
+    dict(dtype=B.TT_BF16, odt=B.TT_BF16, hq=32, hkv=2, d=128, prefix_len=2048, pcap=2048,
+         block_len=32, batch=8, opts=(B.TT_ATTN_MFMA, 4)),
+])
+def test_attn_rejects_invalid(kw):
+    assert attn_call(**kw) == B.TT_EINVAL
+
+
+@pytest.mark.parametrize("kw", [
+    dict(d=96), dict(d=32), dict(opts=(B.TT_ATTN_MFMA, 0)),            # fp32 on MFMA
+    dict(dtype=B.TT_BF16, odt=B.TT_BF16, d=256, opts=(B.TT_ATTN_MFMA, 0)),
+])
+def test_attn_unsupported(kw):
+    assert attn_call(**kw) == B.TT_EUNSUPPORTED
+
+
+def test_attn_empty_is_noop():
+    assert attn_call(batch=0, q=None, out=None) == B.TT_OK
+    assert attn_call(block_len=0, q=None, out=None) == B.TT_OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a GPU")
+def test_attn_valid_call_without_device_reports_enodev():
+    assert attn_call(ws=FAKE, wsb=1 << 24) == B.TT_ENODEV
+    assert tt.lib().tt_unmask_step(FAKE, FAKE, 4, FAKE, FAKE, 1, 16, 1000, None, None, FAKE,
+                                   1 << 20, None) == B.TT_ENODEV
+
+
+def test_attn_workspace_query():
+    # MFMA plan for the decode geometry splits the prefix and needs a workspace.
+    n = tt.attn_workspace_bytes(8, 2048, 32, 32, 2, 128, torch.bfloat16)
+    assert n > 0 and n % 256 == 0
+    assert tt.attn_workspace_bytes(16, 1024, 256, 32, 2, 128, torch.bfloat16) == 0
+    assert tt.attn_workspace_bytes(8, 2048, 32, 32, 2, 128, torch.bfloat16, kv_splits=1) == 0
+    with pytest.raises(ValueError):
+        tt.attn_workspace_bytes(1, 10, 4, 6, 4, 64, torch.float32)
+
+
+def unmask_call(**kw):
+    a = dict(logits=FAKE, mask=FAKE, k=4, tokens=FAKE, mask_out=FAKE, batch=1, L=16, V=1000,
+             conf=None, pred=None, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return tt.lib().tt_unmask_step(a["logits"], a["mask"], a["k"], a["tokens"], a["mask_out"],
+                                   a["batch"], a["L"], a["V"], a["conf"], a["pred"], a["ws"],
+                                   a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(logits=None), dict(mask=None), dict(tokens=None), dict(mask_out=None), dict(k=-1),
+    dict(batch=-1), dict(L=-1), dict(V=0), dict(ws=None), dict(wsb=16),
+])
+def test_unmask_rejects_invalid(kw):
+    assert unmask_call(**kw) == B.TT_EINVAL
+
+
+def test_unmask_limits_and_empty():
+    assert unmask_call(L=1025) == B.TT_EUNSUPPORTED
+    assert unmask_call(batch=0, logits=None, ws=None, wsb=0) == B.TT_OK
+    assert tt.unmask_workspace_bytes(8, 32, 131072) == 8 * 32 * 16 * 16
+    assert tt.unmask_workspace_bytes(1, 16, 1000) == 256
+    with pytest.raises(ValueError):
+        tt.unmask_workspace_bytes(1, 16, 0)
+
+
+def test_unmask_halves_validate():
+    lib = tt.lib()
+    assert lib.tt_unmask_reduce(None, FAKE, 1, 16, 1000, FAKE, 1 << 20, None) == B.TT_EINVAL
+    assert lib.tt_unmask_commit(FAKE, -2, FAKE, FAKE, 1, 16, 1000, None, None, FAKE, 1 << 20,
+                                None) == B.TT_EINVAL
+    assert lib.tt_unmask_commit(FAKE, 2, None, FAKE, 1, 16, 1000, None, None, FAKE, 1 << 20,
+                                None) == B.TT_EINVAL
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        B.lib()

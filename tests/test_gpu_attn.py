@@ -1,0 +1,134 @@
+"""GPU parity of tt_block_attn against the fp64 oracle (element by element on
+small shapes that still span several tiles with ragged tails; sampled heads
+at the full workload sizes, in the launch configuration the benchmark uses)."""
+import numpy as np
+import pytest
+import torch
+
+from denoiser_attention_amd import synth
+from helpers import check_attn, gpu_attn, oracle_attn, say, to_dev
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def small_cfg(**kw):
+    base = synth.get_config("decode_b8_p2048_l32")
+    return base.with_(**kw)
+
+
+def test_tiny_fp32_config():
+    cfg = synth.get_config("tiny_fp32")
+    inp = synth.attn_inputs(cfg, seed=0)
+    got = gpu_attn(inp, DEV)
+    check_attn(got, oracle_attn(inp), "fp32", False, "tiny_fp32")
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_tiny_fp32_splits_and_padding(splits):
+    cfg = synth.get_config("tiny_fp32")
+    inp = synth.attn_inputs(cfg, seed=1, prefix_len=53, prefix_cap=70, block_len=13)
+    got = gpu_attn(inp, DEV, kv_splits=splits)
+    check_attn(got, oracle_attn(inp), "fp32", False, f"fp32 ragged splits={splits}")
+
+
+# (B, Hq, Hkv, L, P, Pcap, D): several query tiles and key tiles, ragged tails.
+SHAPES = [
+    (2, 8, 2, 37, 150, 160, 128),    # M=148 (2 tiles, ragged), 187 keys (ragged)
+    (1, 16, 1, 16, 64, 64, 128),     # M=256 exactly 2 tiles, 80 keys
+    (3, 4, 4, 5, 0, 0, 128),         # no prefix, G=1: M=5 -> shuffle under auto
+    (2, 32, 2, 1, 300, 300, 128),    # single-token block, M=16 (MFMA eligible)
+    (1, 8, 1, 33, 1, 1, 64),         # D=64, one prefix row
+    (2, 6, 3, 20, 96, 96, 64),       # D=64, G=2, M=40
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
+@pytest.mark.parametrize("path", ["auto", "mfma", "shuffle"])
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_bf16_shapes(shape, path, out_f32):
+    B, Hq, Hkv, L, P, Pcap, D = shape
+    cfg = small_cfg(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, prefix_len=P, block_len=L)
+    inp = synth.attn_inputs(cfg, seed=2, prefix_cap=Pcap)
+    if Pcap == 0:
+        inp["k_ctx"] = inp["k_ctx"].reshape(B, Hkv, 0, D)
+    kw = dict(path=path)
+    if out_f32:
+        kw["out_dtype"] = torch.float32
+    got = gpu_attn(inp, DEV, **kw)
+    check_attn(got, oracle_attn(inp), "bf16", not out_f32, f"{shape} {path} f32out={out_f32}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5, 64])
+def test_bf16_forced_splits(splits):
+    cfg = small_cfg(batch=2, prefix_len=700, block_len=24)
+    inp = synth.attn_inputs(cfg, seed=3, prefix_cap=777)
+    got = gpu_attn(inp, DEV, kv_splits=splits, path="mfma")
+    check_attn(got, oracle_attn(inp), "bf16", True, f"splits={splits}")
+
+
+def test_paths_agree_and_deterministic():
+    cfg = small_cfg(batch=2, prefix_len=257, block_len=32)
+    inp = synth.attn_inputs(cfg, seed=4)
+    a = gpu_attn(inp, DEV, path="mfma", out_dtype=torch.float32)
+    b = gpu_attn(inp, DEV, path="mfma", out_dtype=torch.float32)
+    c = gpu_attn(inp, DEV, path="shuffle", out_dtype=torch.float32)
+    assert np.array_equal(a, b), "MFMA path must be bit-deterministic"
+    assert np.abs(a - c).max() < 2e-2
+
+
+def test_guard_bands_and_inputs_untouched():
+    from denoiser_attention_amd import block_attn
+    cfg = small_cfg(batch=2, prefix_len=130, block_len=40)
+    inp = synth.attn_inputs(cfg, seed=5, prefix_cap=150)
+    t = {n: to_dev(inp[n], DEV) for n in ("q", "k_ctx", "v_ctx", "k_blk", "v_blk")}
+    before = {n: v.clone() for n, v in t.items()}
+    n = t["q"].numel()
+    buf = torch.full((n + 2048,), -777.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[1024:1024 + n].view(t["q"].shape)
+    block_attn(t["q"], t["k_ctx"], t["v_ctx"], 130, t["k_blk"], t["v_blk"], inp["scale"], out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:1024] == -777.0) and torch.all(buf[1024 + n:] == -777.0)
+    for k in t:
+        assert torch.equal(t[k], before[k]), f"{k} modified"
+    check_attn(out.float().cpu().numpy().astype(np.float64), oracle_attn(inp), "bf16", True,
+               "guarded")
+
+
+def test_block_permutation_equivariance_on_gpu():
+    cfg = small_cfg(batch=1, prefix_len=100, block_len=32)
+    inp = synth.attn_inputs(cfg, seed=6)
+    base = gpu_attn(inp, DEV, out_dtype=torch.float32)
+    perm = np.random.default_rng(0).permutation(32)
+    p2 = dict(inp)
+    p2["q"] = np.ascontiguousarray(inp["q"][:, :, perm])
+    p2["k_blk"] = np.ascontiguousarray(inp["k_blk"][:, :, perm])
+    p2["v_blk"] = np.ascontiguousarray(inp["v_blk"][:, :, perm])
+    got = gpu_attn(p2, DEV, out_dtype=torch.float32)
+    assert np.abs(got - base[:, :, perm]).max() < 2e-3
+
+
+# Full workload sizes, auto launch configuration (the one the benchmark
+# times); the oracle checks sampled (batch, head) pairs.
+FULL = [
+    ("decode_b8_p2048_l32", {}, [0, 7], [0, 15, 16, 31]),
+    ("block256_b16_p1024", {}, [3, 15], [1, 30]),
+    ("gen8k_b4_l256", dict(prefix_len=512), [0], [0, 31]),
+    ("gen8k_b4_l256", dict(prefix_len=8192), [1], [17]),
+    ("gen8k_b4_l256", dict(prefix_len=16128, prefix_cap=16384), [3], [5]),
+    ("highbatch_b64_p4096_l64", {}, [0, 63], [2, 29]),
+    ("decode_l16", {}, [4], [0, 31]),
+    ("decode_l1", {}, [0, 7], [3, 20]),
+]
+
+
+@pytest.mark.parametrize("name,kw,batches,heads", FULL, ids=[f"{f[0]}-{f[1]}" for f in FULL])
+def test_full_size_sampled(name, kw, batches, heads):
+    cfg = synth.get_config(name)
+    say(f"full-size attention {name} {kw}")
+    inp = synth.attn_inputs(cfg, seed=0, step=0, **kw)
+    got = gpu_attn(inp, DEV)
+    ref = oracle_attn(inp, heads=heads, batches=batches)
+    for (b, h), o in ref.items():
+        check_attn(got[b, h], o, "bf16", True, f"{name} b={b} h={h}")
+    assert np.isfinite(got).all()
