@@ -8,11 +8,13 @@ synthetic-input generator (``synth``).
     unmask_step(logits, mask_state, k, tokens)                     -> (tokens, mask_out)
 """
 from ._binding import (  # noqa: F401
-    LIB_PATH, TTError, attn_workspace_bytes, block_attn, lib, status_string, unmask_commit,
-    unmask_reduce, unmask_step, unmask_workspace_bytes, version,
+    LIB_PATH, Prepared, TTError, attn_workspace_bytes, block_attn, lib, prepare_block_attn,
+    prepare_unmask_commit, prepare_unmask_reduce, status_string, unmask_commit, unmask_reduce,
+    unmask_step, unmask_workspace_bytes, version,
 )
 
 __all__ = [
-    "LIB_PATH", "TTError", "attn_workspace_bytes", "block_attn", "lib", "status_string",
+    "LIB_PATH", "Prepared", "TTError", "attn_workspace_bytes", "block_attn", "lib",
+    "prepare_block_attn", "prepare_unmask_commit", "prepare_unmask_reduce", "status_string",
     "unmask_commit", "unmask_reduce", "unmask_step", "unmask_workspace_bytes", "version",
 ]

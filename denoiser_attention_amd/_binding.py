@@ -228,3 +228,61 @@ def unmask_commit(mask_state, k, tokens, mask_out, vocab, workspace, *, conf_out
                                 vocab, _ptr(conf_out), _ptr(pred_out), _ptr(workspace),
                                 workspace.numel(), _stream(device, stream))
     _check(st, "tt_unmask_commit")
+
+
+class Prepared:
+    """A libtt call whose arguments were validated once; calling it re-issues
+    the same C call (same tensors, same stream).  Keeps per-launch host cost to
+    one ctypes call, e.g. for timing loops or graph capture."""
+
+    __slots__ = ("_fn", "_args", "_what", "keepalive")
+
+    def __init__(self, fn, args, what, keepalive):
+        self._fn, self._args, self._what, self.keepalive = fn, args, what, keepalive
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != TT_OK:
+            raise TTError(st, self._what)
+
+
+def prepare_block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, out, *,
+                       path: str = "auto", kv_splits: int = 0, workspace=None, stream=None):
+    """Validate once (same checks as block_attn) and return a Prepared call."""
+    device = q.device
+    B, Hq, L, D = q.shape
+    Hkv = k_blk.shape[1]
+    Pcap = 0 if k_ctx is None else k_ctx.shape[2]
+    need = attn_workspace_bytes(B, prefix_len, L, Hq, Hkv, D, q.dtype, path, kv_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    # one validating call through the checked path
+    block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, out=out, path=path,
+               kv_splits=kv_splits, workspace=workspace, stream=stream)
+    opts = AttnOpts(_PATHS[path], kv_splits)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    args = (_ptr(q), _ptr(k_ctx), _ptr(v_ctx), prefix_len, _ptr(k_blk), _ptr(v_blk), L, Hq, Hkv,
+            D, float(scale), _ptr(out), B, Pcap, _dtype_code(q.dtype), _dtype_code(out.dtype),
+            _ptr(workspace), ws_bytes, _stream(device, stream), ctypes.byref(opts))
+    keep = (q, k_ctx, v_ctx, k_blk, v_blk, out, workspace, opts)
+    return Prepared(lib().tt_block_attn_ex, args, "tt_block_attn", keep)
+
+
+def prepare_unmask_reduce(logits, mask_state, workspace, *, stream=None):
+    device, B, L = _unmask_checks(logits, mask_state, None, None, None, None)
+    V = logits.shape[2]
+    _require(workspace.numel() >= unmask_workspace_bytes(B, L, V), "workspace too small")
+    args = (_ptr(logits), _ptr(mask_state), B, L, V, _ptr(workspace), workspace.numel(),
+            _stream(device, stream))
+    return Prepared(lib().tt_unmask_reduce, args, "tt_unmask_reduce",
+                    (logits, mask_state, workspace))
+
+
+def prepare_unmask_commit(mask_state, k, tokens, mask_out, vocab, workspace, *, conf_out=None,
+                          pred_out=None, stream=None):
+    device, B, L = _unmask_checks(None, mask_state, tokens, mask_out, conf_out, pred_out)
+    _require(workspace.numel() >= unmask_workspace_bytes(B, L, vocab), "workspace too small")
+    args = (_ptr(mask_state), int(k), _ptr(tokens), _ptr(mask_out), B, L, vocab, _ptr(conf_out),
+            _ptr(pred_out), _ptr(workspace), workspace.numel(), _stream(device, stream))
+    return Prepared(lib().tt_unmask_commit, args, "tt_unmask_commit",
+                    (mask_state, tokens, mask_out, workspace, conf_out, pred_out))

@@ -10,61 +10,76 @@
 //   * Grouped-query packing: the G = Hq/Hkv query heads that read one KV head
 //     are contiguous in q[B,Hq,L,D], so the G*L query rows of a (batch, kv
 //     head) pair form one contiguous matrix of M = G*L rows.  A workgroup takes
-//     128 of those rows (4 waves x 32) and streams the pair's keys once for all
-//     of them, so each K/V byte fetched from HBM feeds G*L rows.
-//   * Key tiles of 64 rows are fetched with 128-bit global loads into
-//     registers, then written to a double-buffered LDS tile: K row-major, V
-//     transposed (V^T, with keys permuted inside each 16-key group to match the
-//     MFMA operand order below).  One barrier per tile.
+//     128 of them (4 waves x 32) and streams the pair's keys once for all of
+//     them: every K/V byte fetched from HBM feeds G*L query rows.
+//   * K/V stream: 32-key tiles go straight from global memory into a ring of
+//     NS LDS stages with 16-byte direct-to-LDS loads (no register staging, no
+//     LDS store instructions); NS-1 tiles are in flight while one is consumed.
+//     Waits are explicit vmcnt counts and raw barriers, so that loads of later
+//     stages stay in flight across the barrier.
+//   * LDS layout: K and V tiles are row-major with the 16-byte chunks of each
+//     row XOR-swizzled by a function of the row, chosen so that both operand
+//     read patterns below hit distinct banks.
 //   * Scores are computed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q held in registers), so
-//     that in the accumulator layout each lane owns ONE query row and 16 keys
-//     of each 32-key block; the other 16 keys of that row sit in lane ^ 32.
-//     Softmax statistics are therefore per lane, with one cross-half exchange
-//     for the tile maximum.
-//   * Online softmax in base 2 with the scale folded into the exponent.  The
-//     running maximum is refreshed lazily: the accumulators are rescaled only
-//     when a tile's maximum exceeds the reference by more than 2^8, so
-//     unnormalised weights stay below 256 (exact in the final normalisation).
-//   * O^T += V^T P^T with the same MFMA: A = V^T from LDS, B = P (bf16) taken
-//     straight from the score accumulators, so P never leaves registers.
-//   * Optional key-range splitting (split-KV) when there are too few query
-//     tiles to fill 256 CUs; each split writes an fp32 partial output and its
+//     v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q in registers): in the
+//     accumulator layout each lane owns ONE query row and 16 of the tile's 32
+//     keys (the other 16 sit in lane ^ 32), so the softmax statistics are
+//     per lane plus one cross-half exchange.
+//   * Online softmax in base 2 with the scale folded into the exponent; the
+//     reference maximum is refreshed lazily (accumulators are rescaled only
+//     when a tile maximum exceeds it by more than 2^8, so unnormalised weights
+//     stay below 256; the final normalisation makes this exact).
+//   * O^T += V^T P^T with the same MFMA: P (bf16) comes straight from the score
+//     accumulators; the V^T operand is read from the row-major V tile with the
+//     transposing LDS read ds_read_b64_tr_b16 (each 16-lane group turns a
+//     4-key x 16-column block into 16 lanes x 4 keys).
+//   * Optional key-range splitting (split-KV) when the query tiles alone
+//     cannot fill 256 CUs; each split writes an fp32 partial output and its
 //     base-2 log-sum-exp, merged by attn_merge_kernel.
 //   * Workgroup ids are remapped so that each XCD (own L2) receives a
 //     contiguous range of query tiles of the same (pair, split).
+#include <type_traits>
+
 #include "tt_internal.h"
 
 namespace tt {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int BM = kAttnMfmaBM;   // 128 packed query rows per workgroup
-constexpr int BN = kAttnMfmaBN;   // 64 keys per tile
+constexpr int BN = kAttnMfmaBN;   // 32 keys per pipeline stage
 constexpr float kLazyRescale = 8.0f;  // log2 headroom before the max is refreshed
 static_assert(BM == 32 * kWaves, "one 32-row MFMA tile per wave");
+static_assert(BN == 32, "the score tile is one 32x32 MFMA block");
 
 template <int D>
 struct Lay {
-  static constexpr int KS = D + 8;       // K tile row stride, bf16 elements (pad: bank spread)
-  static constexpr int VS = BN + 8;      // V^T tile row stride
-  static constexpr int K_EL = BN * KS;
-  static constexpr int V_EL = D * VS;
-  static constexpr int BUF_EL = K_EL + V_EL;
-  static constexpr int CH = D / 8;       // 16-byte chunks per K/V row
-  static constexpr int DS = D / 16;      // MFMA k-steps over head_dim (16 per step)
-  static constexpr int DB = D / 32;      // 32-wide blocks of output columns
-  static constexpr int K_PER_THREAD = BN * CH / kThreads;
-  static constexpr int V_ITEMS = CH * (BN / 4);   // (d-chunk, 4-key quad) items
-  static_assert(BN * CH % kThreads == 0, "K tile chunks must divide evenly");
-  static_assert(V_ITEMS <= kThreads, "one V item per thread at most");
+  static constexpr int CH = D / 8;           // 16-byte chunks per K/V row
+  static constexpr int ROWB = D * 2;         // bytes per K/V row
+  static constexpr int TILE_B = BN * ROWB;   // one K (or V) tile
+  static constexpr int STAGE_B = 2 * TILE_B; // K tile then V tile
+  static constexpr int DS = D / 16;          // MFMA k-steps over head_dim
+  static constexpr int DB = D / 32;          // 32-wide blocks of output columns
+  static constexpr int LOADS = BN * CH / kThreads;  // 16-byte loads per thread per tile (K or V)
+  static_assert(BN * CH % kThreads == 0, "tile chunks must divide evenly");
+  // Swizzle: chunk c of row r lives in slot c ^ f(r).
+  // K is read as 16 rows x one chunk per 16 lanes: f_k spreads 16 rows over all banks.
+  __device__ static int fk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  // V is read by the transposing load as 4 rows x 32 bytes per 16 lanes.
+  __device__ static int fv(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 __device__ __forceinline__ int xcd_remap(int i, int n) {
@@ -76,43 +91,83 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
   return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
 }
 
-__device__ __forceinline__ uint32_t half_of(uint32_t w, int hi) {
-  return hi ? (w >> 16) : (w & 0xFFFFu);
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// also drain the loads that must stay in flight).  The memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// One 16-byte direct-to-LDS load per lane: lane i's 16 bytes land at LDS byte
+// address lds + 16*i (lds is the same for the whole wave and goes in M0).  It
+// is issued from asm so that the compiler, which cannot tell these writes
+// apart from later LDS reads, does not drain them before every LDS read; the
+// explicit vmcnt waits and barriers below order them instead.  The asm has no
+// register outputs.
+__device__ __forceinline__ void dma16(const char* g, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 
-template <int D>
-__device__ __forceinline__ const u32x4* key_row(const uint16_t* ctx, const uint16_t* blk,
-                                                int j, int P) {
-  return reinterpret_cast<const u32x4*>(j < P ? ctx + (size_t)j * D
-                                              : blk + (size_t)(j - P) * D);
+// The same load with a wave-uniform 64-bit base in SGPRs and a per-lane
+// 32-bit byte offset.
+__device__ __forceinline__ void dma16_s(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnParams p, int m_tiles,
-                                                             int n_blocks) {
+// Maximum of x over lanes l and l ^ 32, for every lane l.  v_permlane32_swap
+// exchanges the two 32-lane halves between its two results, so together they
+// hold both halves' values for each lane.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(x, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
+// Marks a register value as used (forces its load to complete here).
+__device__ __forceinline__ void consume(bf16x8 v) { asm volatile("" ::"v"(v)); }
+
+template <int D, int NS>
+__device__ __forceinline__ void wait_tiles(int n_after) {
+  constexpr int per = 2 * Lay<D>::LOADS;
+  static_assert(NS - 2 <= 3, "extend the switch for deeper rings");
+  switch (n_after) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<per>(); break;
+    case 2: wait_vmcnt<2 * per>(); break;
+    default: wait_vmcnt<3 * per>(); break;
+  }
+}
+
+template <int D, int NS, bool OUT_BF16, bool POS_SCALE>
+__global__ __launch_bounds__(kThreads, 2)
+void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   using L = Lay<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::BUF_EL];
+  __shared__ __attribute__((aligned(1024))) char smem[NS * L::STAGE_B];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 31, hh = lane >> 5;
+  const int lr = lane & 31, hh = lane >> 5;     // MFMA row/column lane, lane half
+  const int grp = lane >> 4, gi = lane & 15;    // 16-lane group, index in group
 
   int logical = xcd_remap(blockIdx.x, n_blocks);
   const int mt = logical % m_tiles;
   logical /= m_tiles;
   const int split = logical % p.splits;
   const int pair = logical / p.splits;       // b * Hkv + kv head
-  const int b = pair / p.Hkv, kvh = pair - (pair / p.Hkv) * p.Hkv;
+  const int b = pair / p.Hkv, kvh = pair - b * p.Hkv;
 
   const int n_keys = p.n_keys, P = p.P;
   const int n_tiles = (n_keys + BN - 1) / BN;
   const int t_begin = split * p.tiles_per_split;
   const int t_end = min(n_tiles, t_begin + p.tiles_per_split);
 
-  const uint16_t* kc = static_cast<const uint16_t*>(p.k_ctx) + (size_t)pair * p.Pcap * D;
-  const uint16_t* vc = static_cast<const uint16_t*>(p.v_ctx) + (size_t)pair * p.Pcap * D;
-  const uint16_t* kb = static_cast<const uint16_t*>(p.k_blk) + (size_t)pair * p.L * D;
-  const uint16_t* vb = static_cast<const uint16_t*>(p.v_blk) + (size_t)pair * p.L * D;
+  const char* kc = static_cast<const char*>(p.k_ctx) + (size_t)pair * p.Pcap * L::ROWB;
+  const char* vc = static_cast<const char*>(p.v_ctx) + (size_t)pair * p.Pcap * L::ROWB;
+  const char* kb = static_cast<const char*>(p.k_blk) + (size_t)pair * p.L * L::ROWB;
+  const char* vb = static_cast<const char*>(p.v_blk) + (size_t)pair * p.L * L::ROWB;
 
   // First row of this pair in the flattened [B*Hq*L] row space.
   const size_t row_base = ((size_t)b * p.Hq + (size_t)kvh * p.G) * p.L;
@@ -128,164 +183,194 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnParams p, int m
                                                       (row_base + (row_ok ? r_local : 0)) * D);
 #pragma unroll
     for (int s = 0; s < L::DS; ++s) {
-      u32x4 v = row_ok ? src[2 * s + hh] : u32x4{0, 0, 0, 0};
+      const u32x4 v = row_ok ? src[2 * s + hh] : u32x4{0, 0, 0, 0};
       qf[s] = __builtin_bit_cast(bf16x8, v);
     }
+    // Consume Q here so that its load wait is placed before the K/V stream
+    // starts (and not inside the pipelined loop).
+#pragma unroll
+    for (int s = 0; s < L::DS; ++s) consume(qf[s]);
   }
 
-  // Register staging of one K/V tile.
-  u32x4 kreg[L::K_PER_THREAD];
-  u32x4 vreg[4];
+  // LDS byte address of the ring.
+  const uint32_t smem_u32 = (uint32_t)(uintptr_t)(lds_char*)smem;
 
-  auto load_tile = [&](int t) {
+  // Direct-to-LDS loads of tile t into ring slot `slot`.  Thread tid fills
+  // 16-byte slot i*256 + tid of each K and V tile: row r_i, slot column q_i,
+  // holding global chunk q_i ^ f(r_i).  A tile lying wholly in the cache or
+  // wholly in the block uses a uniform base and per-thread constant offsets;
+  // the tile that straddles the two (or runs past the end) computes each row's
+  // address, with rows past the end loading the last valid row (their scores
+  // are masked).
+  uint32_t koff[L::LOADS], voff[L::LOADS];
+  int rrow[L::LOADS];
+#pragma unroll
+  for (int i = 0; i < L::LOADS; ++i) {
+    const int s = i * kThreads + tid;
+    const int r = s / L::CH, q = s % L::CH;
+    rrow[i] = r;
+    koff[i] = r * L::ROWB + ((q ^ L::fk(r)) << 4);
+    voff[i] = r * L::ROWB + ((q ^ L::fv(r)) << 4);
+  }
+  auto issue = [&](int t, int slot) {
+    const uint32_t kst = smem_u32 + slot * L::STAGE_B;
+    const uint32_t vst = kst + L::TILE_B;
     const int key0 = t * BN;
-#pragma unroll
-    for (int i = 0; i < L::K_PER_THREAD; ++i) {
-      const int id = tid + i * kThreads;
-      const int row = id / L::CH, c = id % L::CH;
-      const int j = key0 + row;
-      kreg[i] = j < n_keys ? key_row<D>(kc, kb, j, P)[c] : u32x4{0, 0, 0, 0};
+    const char *kbase, *vbase;
+    bool uniform = true;
+    if (key0 + BN <= P) {
+      kbase = kc + (size_t)key0 * L::ROWB;
+      vbase = vc + (size_t)key0 * L::ROWB;
+    } else if (key0 >= P && key0 + BN <= n_keys) {
+      kbase = kb + (size_t)(key0 - P) * L::ROWB;
+      vbase = vb + (size_t)(key0 - P) * L::ROWB;
+    } else {
+      uniform = false;
+      kbase = vbase = nullptr;
     }
-    if (tid < L::V_ITEMS) {
-      const int c = tid % L::CH, quad = tid / L::CH;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = key0 + 4 * quad + i;
-        vreg[i] = j < n_keys ? key_row<D>(vc, vb, j, P)[c] : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < L::LOADS; ++i) {
+      const uint32_t wofs = (i * kThreads + wave * 64) * 16;   // wave-uniform destination
+      if (uniform) {
+        dma16_s(kbase, koff[i], kst + wofs);
+        dma16_s(vbase, voff[i], vst + wofs);
+      } else {
+        const int j = min(key0 + rrow[i], n_keys - 1);
+        const size_t rel = (size_t)rrow[i] * L::ROWB;
+        const char* krow = j < P ? kc + (size_t)j * L::ROWB : kb + (size_t)(j - P) * L::ROWB;
+        const char* vrow = j < P ? vc + (size_t)j * L::ROWB : vb + (size_t)(j - P) * L::ROWB;
+        dma16(krow + (koff[i] - rel), kst + wofs);
+        dma16(vrow + (voff[i] - rel), vst + wofs);
       }
     }
   };
 
-  auto store_tile = [&](int buf) {
-    uint16_t* Ks = smem + buf * L::BUF_EL;
-    uint16_t* Vt = Ks + L::K_EL;
+  // Per-lane LDS offsets.  K operand: row lr, chunk 2s + hh.
+  const int k_row_off = lr * L::ROWB;
+  const int fkl = L::fk(lr);
+  // V^T operand through the transposing read: as a source lane of its 16-lane
+  // group this lane points at V[k0 + gi/4][d0 + 4*(gi%4) .. +3], with
+  // k0 = 4*(grp/2) (+16 per k-step, +8 for the second half) and
+  // d0 = 32*db + 16*(grp%2).
+  int vofs[L::DB];
 #pragma unroll
-    for (int i = 0; i < L::K_PER_THREAD; ++i) {
-      const int id = tid + i * kThreads;
-      const int row = id / L::CH, c = id % L::CH;
-      *reinterpret_cast<u32x4*>(Ks + row * L::KS + 8 * c) = kreg[i];
-    }
-    if (tid < L::V_ITEMS) {
-      const int c = tid % L::CH, quad = tid / L::CH;
-      const int qq = quad & 3;
-      // Position of keys 4qq..4qq+3 inside their 16-key group: the MFMA B
-      // operand of P holds, for lane half h and element e, the key
-      // (e < 4 ? 4h + e : 8 + 4h + e - 4); store V^T in that order.
-      const int pos = (quad >> 2) * 16 + (qq & 1) * 8 + (qq >> 1) * 4;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1, hi = e & 1;
-        u32x2 pk;
-        pk.x = half_of(vreg[0][w], hi) | (half_of(vreg[1][w], hi) << 16);
-        pk.y = half_of(vreg[2][w], hi) | (half_of(vreg[3][w], hi) << 16);
-        *reinterpret_cast<u32x2*>(Vt + (8 * c + e) * L::VS + pos) = pk;
-      }
-    }
-  };
+  for (int db = 0; db < L::DB; ++db) {
+    const int key = 4 * (grp >> 1) + (gi >> 2);
+    const int c = 4 * db + 2 * (grp & 1) + ((gi & 3) >> 1);
+    vofs[db] = key * L::ROWB + ((c ^ L::fv(gi >> 2)) << 4) + ((gi & 1) << 3);
+  }
 
   f32x16 oacc[L::DB];
 #pragma unroll
   for (int db = 0; db < L::DB; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY;   // reference max (base-2 scaled units)
-  float l_run = 0.0f;        // this lane's partial row sum (its 32 keys per tile)
+  float l_run = 0.0f;        // this lane's partial row sum (its 16 keys of each tile)
   const float c = p.scale_log2;
 
-  load_tile(t_begin);
-  store_tile(0);
-  __syncthreads();
+  // One 32-key tile: scores, online softmax, P.V.  TAIL instantiation masks the
+  // keys past the end of the sequence (only the last tile can need it).
+  auto tile = [&](auto tail_tag, int t, int slot) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const char* Ks = smem + slot * L::STAGE_B;
+    const char* Vs = Ks + L::TILE_B;
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    const bool has_next = t + 1 < t_end;
-    if (has_next) load_tile(t + 1);
-
-    if (wave_active) {
-      const uint16_t* Ks = smem + buf * L::BUF_EL;
-      const uint16_t* Vt = Ks + L::K_EL;
-
-      // S^T = K Q^T for two 32-key blocks.
-      f32x16 sacc[2];
+    // S^T = K Q^T over the tile's 32 keys.
+    f32x16 sacc = f32x16{};
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        sacc[kb2] = f32x16{};
-        const uint16_t* krow = Ks + (kb2 * 32 + lr) * L::KS + 8 * hh;
-#pragma unroll
-        for (int s = 0; s < L::DS; ++s) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * s);
-          sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb2], 0, 0, 0);
-        }
-      }
-
-      // Scale to base-2 units; mask keys past the end of the sequence.
-      const int key0 = t * BN;
-      const bool tail = key0 + BN > n_keys;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = sacc[kb2][r] * c;
-          if (tail) {
-            const int key = key0 + kb2 * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key >= n_keys) v = -INFINITY;
-          }
-          sacc[kb2][r] = v;
-        }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-
-      // Lazy refresh of the reference max (uniform branch over the wave).
-      const bool need = mx > m_run + kLazyRescale;
-      if (__any(need)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < L::DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        m_run = m_new;
-      }
-
-      // P = exp2(S - m) in bf16, straight into MFMA B fragments.
-      bf16x8 pf[4];
-      float psum = 0.0f;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(sacc[kb2][r] - m_run);
-          psum += pv;
-          pf[kb2 * 2 + (r >> 3)][r & 7] = (__bf16)pv;
-        }
-      l_run += psum;
-
-      // O^T += V^T P^T.
-#pragma unroll
-      for (int db = 0; db < L::DB; ++db) {
-        const uint16_t* vrow = Vt + (db * 32 + lr) * L::VS + 8 * hh;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + 16 * ks);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], oacc[db], 0, 0, 0);
-        }
-      }
+    for (int s = 0; s < L::DS; ++s) {
+      const bf16x8 a =
+          *reinterpret_cast<const bf16x8*>(Ks + k_row_off + (((2 * s + hh) ^ fkl) << 4));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc, 0, 0, 0);
     }
 
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
+    // Accumulator register r holds key 8*(r/4) + 4*hh + r%4 of the tile.
+    const int key0 = t * BN;
+    auto valid = [&](int r) { return !TAIL || key0 + 8 * (r >> 2) + 4 * hh + (r & 3) < n_keys; };
+    float mraw = POS_SCALE ? -INFINITY : INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float v = valid(r) ? sacc[r] : (POS_SCALE ? -INFINITY : INFINITY);
+      mraw = POS_SCALE ? fmaxf(mraw, v) : fminf(mraw, v);
+    }
+    float mx = mraw * c;
+    mx = pair_max(mx);
+
+    // Lazy refresh of the reference max (uniform branch over the wave).
+    if (__any(mx > m_run + kLazyRescale)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < L::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
+    }
+
+    // P = exp2(S*c - m) rounded to bf16, straight into MFMA B fragments; the
+    // row sum adds exactly the bf16 weights that enter P.V (packed dot with 1).
+    bf16x8 pf[2];
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -m_run));
+      float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], c, -m_run));
+      if (!valid(r)) p0 = 0.0f;
+      if (!valid(r + 1)) p1 = 0.0f;
+      const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+      pf[r >> 3][r & 7] = pk[0];
+      pf[r >> 3][(r & 7) + 1] = pk[1];
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, one2, l_run, false);
+    }
+
+    // O^T += V^T P^T: two 16-key k-steps per 32-wide block of output columns.
+    // Element j of the V^T operand of k-step ks is key 16*ks + (j < 4 ? 4*hh + j
+    // : 8 + 4*hh + j - 4): the first transposing read covers j < 4, the second
+    // (8 rows further) j >= 4.
+#pragma unroll
+    for (int db = 0; db < L::DB; ++db) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const lds_char* vp = (const lds_char*)(Vs + vofs[db] + ks * 16 * L::ROWB);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * L::ROWB));
+        const i16x8 a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16),
+                                                            pf[ks], oacc[db], 0, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (t_begin + s < t_end) issue(t_begin + s, s);
+
+  // Ring bookkeeping for tile t: wait for it, make it visible to the whole
+  // workgroup (this also retires every read of the slot refilled next), and
+  // start loading tile t + NS - 1 into the slot of tile t - 1.
+  auto advance = [&](int t) {
+    wait_tiles<D, NS>(min(NS - 2, t_end - 1 - t));
+    barrier();
+    if (t + NS - 1 < t_end) issue(t + NS - 1, (t - t_begin + NS - 1) % NS);
+  };
+  // Only the last tile of the key range can run past the end of the sequence;
+  // it is peeled off so that the steady-state loop carries no masking.
+  const int t_full = (t_end * BN > n_keys) ? t_end - 1 : t_end;
+  for (int t = t_begin; t < t_full; ++t) {
+    advance(t);
+    if (wave_active) tile(std::false_type{}, t, (t - t_begin) % NS);
+  }
+  if (t_full < t_end) {
+    advance(t_full);
+    if (wave_active) tile(std::true_type{}, t_full, (t_full - t_begin) % NS);
   }
 
   if (!wave_active) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!row_ok) return;
   const size_t grow = row_base + r_local;
+  const float inv = 1.0f / l_tot;
   if (p.splits == 1) {
-    const float inv = 1.0f / l_tot;
 #pragma unroll
     for (int db = 0; db < L::DB; ++db)
 #pragma unroll
@@ -307,7 +392,6 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnParams p, int m
       }
   } else {
     const size_t rows_total = (size_t)p.B * p.Hq * p.L;
-    const float inv = 1.0f / l_tot;
     float* po = p.part_o + ((size_t)split * rows_total + grow) * D;
 #pragma unroll
     for (int db = 0; db < L::DB; ++db)
@@ -322,23 +406,32 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnParams p, int m
   }
 }
 
-template <int D, bool OUT_BF16>
+constexpr int kStages = 4;
+
+template <int D, bool OUT_BF16, bool POS>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   const int m_tiles = (p.M + BM - 1) / BM;
   const long long n = (long long)m_tiles * p.splits * p.B * p.Hkv;
   if (n <= 0 || n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_mfma_kernel<D, OUT_BF16>), dim3((unsigned)n), dim3(kThreads), 0,
-                     stream, p, m_tiles, (int)n);
+  hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, OUT_BF16, POS>), dim3((unsigned)n),
+                     dim3(kThreads), 0, stream, p, m_tiles, (int)n);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
+  const bool ob = p.out_bf16 && p.splits == 1;
+  const bool pos = p.scale_log2 >= 0.0f;
+  if (ob) return pos ? launch_typed<D, true, true>(p, stream) : launch_typed<D, true, false>(p, stream);
+  return pos ? launch_typed<D, false, true>(p, stream) : launch_typed<D, false, false>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attn_mfma(const AttnParams& p, hipStream_t stream) {
-  const bool ob = p.out_bf16 && p.splits == 1;
   switch (p.D) {
-    case 64: return ob ? launch_typed<64, true>(p, stream) : launch_typed<64, false>(p, stream);
-    case 128: return ob ? launch_typed<128, true>(p, stream) : launch_typed<128, false>(p, stream);
+    case 64: return launch_d<64>(p, stream);
+    case 128: return launch_d<128>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

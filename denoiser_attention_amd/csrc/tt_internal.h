@@ -27,7 +27,7 @@ struct AttnParams {
 };
 
 // Keys per tile of the MFMA kernel and packed query rows per workgroup.
-constexpr int kAttnMfmaBN = 64;
+constexpr int kAttnMfmaBN = 32;
 constexpr int kAttnMfmaBM = 128;
 // Keys per tile (one tile per split iteration) and rows per workgroup of the
 // wavefront-shuffle kernel.

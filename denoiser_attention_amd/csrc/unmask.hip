@@ -17,7 +17,8 @@
 // topk_commit_kernel -- one workgroup per sequence: merges the chunk triples of
 //   each masked position in chunk order, forms the confidence, ranks every
 //   masked position by counting the masked positions ahead of it in the order
-//   (confidence descending, position ascending) and commits rank < k.
+//   (confidence descending, position ascending), 4 confidences per LDS read,
+//   and commits rank < k.
 #include <climits>
 
 #include "tt_internal.h"
@@ -31,6 +32,7 @@ constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kVecPerThread = kVocabChunk / (kThreads * 4);      // 8 float4 loads
 constexpr int kScalarPerThread = kVocabChunk / kThreads;         // 32 scalar loads
+constexpr int kMergeBatch = 16;                                  // partial loads in flight per position
 static_assert(kVocabChunk % (kThreads * 4) == 0, "chunk must be a multiple of 1024");
 
 struct Triple {
@@ -141,51 +143,67 @@ __global__ __launch_bounds__(kThreads) void vocab_reduce_kernel(UnmaskParams p) 
 }
 
 __global__ __launch_bounds__(kThreads) void topk_commit_kernel(UnmaskParams p) {
-  __shared__ float s_conf[kUnmaskMaxL];
+  // Confidences of the sequence; positions that are not masked hold -2, which
+  // never compares >= a real confidence (those lie in (0, 1]).  The array is
+  // padded to a multiple of 4 so that the rank loop reads 16 bytes at a time.
+  __shared__ __attribute__((aligned(16))) float s_conf[kUnmaskMaxL];
   __shared__ int s_pred[kUnmaskMaxL];
-  __shared__ unsigned char s_mask[kUnmaskMaxL];
 
   const int b = blockIdx.x;
   const int L = p.L;
+  const int L4 = (L + 3) >> 2;
   const int tid = threadIdx.x;
   const size_t row0 = (size_t)b * L;
 
   // Every mask flag of the sequence is read before any is written, so
   // mask_out may alias mask_state.
-  for (int l = tid; l < L; l += kThreads) {
-    const size_t row = row0 + l;
-    const bool masked = p.mask_state[row] != 0;
-    float conf = -1.0f;
+  for (int l = tid; l < 4 * L4; l += kThreads) {
+    float conf = -2.0f;
     int pred = -1;
-    if (masked) {
-      const VocabPartial* pp = p.partials + row * (size_t)p.n_chunks;
+    if (l < L && p.mask_state[row0 + l] != 0) {
+      const VocabPartial* pp = p.partials + (row0 + l) * (size_t)p.n_chunks;
       Triple t{-INFINITY, INT_MAX, 0.0f};
-      for (int c = 0; c < p.n_chunks; ++c) {
-        const VocabPartial q = pp[c];
-        t = combine(t, Triple{q.m, q.arg, q.s});
+      // Issue a batch of independent 16-byte loads, then merge in chunk order.
+      for (int c0 = 0; c0 < p.n_chunks; c0 += kMergeBatch) {
+        VocabPartial q[kMergeBatch];
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i)
+          if (c0 + i < p.n_chunks) q[i] = pp[c0 + i];
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i)
+          if (c0 + i < p.n_chunks) t = combine(t, Triple{q[i].m, q[i].arg, q[i].s});
       }
       conf = 1.0f / t.s;
       pred = t.arg;
     }
     s_conf[l] = conf;
-    s_pred[l] = pred;
-    s_mask[l] = masked ? 1 : 0;
+    if (l < L) s_pred[l] = pred;
   }
   __syncthreads();
 
+  // rank(l) = #{masked j : conf_j > conf_l, or conf_j == conf_l and j < l};
+  // commit when rank < k.
+  const f32x4* c4 = reinterpret_cast<const f32x4*>(s_conf);
   for (int l = tid; l < L; l += kThreads) {
     const size_t row = row0 + l;
-    bool commit = false;
-    if (s_mask[l] && p.k > 0) {
-      const float c = s_conf[l];
-      int ahead = 0;
-      for (int j = 0; j < L && ahead < p.k; ++j)
-        ahead += (s_mask[j] && (s_conf[j] > c || (s_conf[j] == c && j < l))) ? 1 : 0;
-      commit = ahead < p.k;
+    const float c = s_conf[l];
+    const bool masked = c > -1.0f;
+    int ahead = 0;
+    if (masked && p.k > 0) {
+#pragma unroll 4
+      for (int j4 = 0; j4 < L4; ++j4) {
+        const f32x4 v = c4[j4];
+        const int j = 4 * j4;
+        ahead += (v.x > c || (v.x == c && j + 0 < l)) ? 1 : 0;
+        ahead += (v.y > c || (v.y == c && j + 1 < l)) ? 1 : 0;
+        ahead += (v.z > c || (v.z == c && j + 2 < l)) ? 1 : 0;
+        ahead += (v.w > c || (v.w == c && j + 3 < l)) ? 1 : 0;
+      }
     }
+    const bool commit = masked && ahead < p.k;
     if (commit) p.tokens_out[row] = s_pred[l];
-    p.mask_out[row] = (s_mask[l] && !commit) ? 1 : 0;
-    if (p.conf_out) p.conf_out[row] = s_conf[l];
+    p.mask_out[row] = (masked && !commit) ? 1 : 0;
+    if (p.conf_out) p.conf_out[row] = masked ? c : -1.0f;
     if (p.pred_out) p.pred_out[row] = s_pred[l];
   }
 }
