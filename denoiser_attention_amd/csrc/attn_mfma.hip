@@ -132,7 +132,7 @@ __device__ __forceinline__ void consume(bf16x8 v) { asm volatile("" ::"v"(v)); }
 template <int D, int NS>
 __device__ __forceinline__ void wait_tiles(int n_after) {
   constexpr int per = 2 * Lay<D>::LOADS;
-  static_assert(NS - 2 <= 3, "extend the switch for deeper rings");
+  static_assert(NS >= 3 && NS - 3 <= 3, "ring depth outside the waits below");
   switch (n_after) {
     case 0: wait_vmcnt<0>(); break;
     case 1: wait_vmcnt<per>(); break;
@@ -148,7 +148,8 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   __shared__ __attribute__((aligned(1024))) char smem[NS * L::STAGE_B];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int lr = lane & 31, hh = lane >> 5;     // MFMA row/column lane, lane half
   const int grp = lane >> 4, gi = lane & 15;    // 16-lane group, index in group
 
@@ -267,14 +268,9 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   float l_run = 0.0f;        // this lane's partial row sum (its 16 keys of each tile)
   const float c = p.scale_log2;
 
-  // One 32-key tile: scores, online softmax, P.V.  TAIL instantiation masks the
-  // keys past the end of the sequence (only the last tile can need it).
-  auto tile = [&](auto tail_tag, int t, int slot) {
-    constexpr bool TAIL = decltype(tail_tag)::value;
+  // S^T = K Q^T over the 32 keys of the tile in ring slot `slot`.
+  auto qk = [&](int slot) {
     const char* Ks = smem + slot * L::STAGE_B;
-    const char* Vs = Ks + L::TILE_B;
-
-    // S^T = K Q^T over the tile's 32 keys.
     f32x16 sacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < L::DS; ++s) {
@@ -282,7 +278,15 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
           *reinterpret_cast<const bf16x8*>(Ks + k_row_off + (((2 * s + hh) ^ fkl) << 4));
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc, 0, 0, 0);
     }
+    return sacc;
+  };
 
+  // Online softmax of tile t's scores and O^T += V^T P^T.  The TAIL
+  // instantiation masks the keys past the end of the sequence (only the last
+  // tile can need it).
+  auto softmax_pv = [&](auto tail_tag, const f32x16& sacc, int t, int slot) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const char* Vs = smem + slot * L::STAGE_B + L::TILE_B;
     // Accumulator register r holds key 8*(r/4) + 4*hh + r%4 of the tile.
     const int key0 = t * BN;
     auto valid = [&](int r) { return !TAIL || key0 + 8 * (r >> 2) + 4 * hh + (r & 3) < n_keys; };
@@ -341,29 +345,40 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     }
   };
 
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (t_begin + s < t_end) issue(t_begin + s, s);
-
-  // Ring bookkeeping for tile t: wait for it, make it visible to the whole
-  // workgroup (this also retires every read of the slot refilled next), and
-  // start loading tile t + NS - 1 into the slot of tile t - 1.
-  auto advance = [&](int t) {
-    wait_tiles<D, NS>(min(NS - 2, t_end - 1 - t));
+  // Software pipeline over the key tiles: while the vector units run the
+  // softmax of tile t, the matrix cores already compute the scores of tile
+  // t + 1.  Ring occupancy during iteration t: tile t (its V is read), tile t+1
+  // (its K is read), tiles t+2 .. t+NS-2 in flight; tile t+NS-1 is issued into
+  // the slot of tile t-1, which every wave has finished with once it passes
+  // the barrier of iteration t.
+  static_assert((NS & (NS - 1)) == 0, "ring depth must be a power of two");
+  auto slot_of = [&](int u) { return (u - t_begin) & (NS - 1); };
+  // Wait until tile u has landed for the whole workgroup, then refill the slot
+  // of tile u-2 with tile u+NS-2.
+  auto advance = [&](int u) {
+    wait_tiles<D, NS>(min(NS - 3, t_end - 1 - u));
     barrier();
-    if (t + NS - 1 < t_end) issue(t + NS - 1, (t - t_begin + NS - 1) % NS);
+    if (u + NS - 2 < t_end) issue(u + NS - 2, slot_of(u + NS - 2));
   };
-  // Only the last tile of the key range can run past the end of the sequence;
-  // it is peeled off so that the steady-state loop carries no masking.
-  const int t_full = (t_end * BN > n_keys) ? t_end - 1 : t_end;
-  for (int t = t_begin; t < t_full; ++t) {
-    advance(t);
-    if (wave_active) tile(std::false_type{}, t, (t - t_begin) % NS);
+#pragma unroll
+  for (int s = 0; s < NS - 2; ++s)
+    if (t_begin + s < t_end) issue(t_begin + s, s);
+  // Waves whose rows all lie past M run the same instruction stream on zero Q
+  // rows (no branch in the loop) and store nothing.
+  advance(t_begin);
+  f32x16 s_cur = qk(slot_of(t_begin));
+#pragma unroll 2
+  for (int t = t_begin; t + 1 < t_end; ++t) {
+    advance(t + 1);
+    const f32x16 s_next = qk(slot_of(t + 1));
+    softmax_pv(std::false_type{}, s_cur, t, slot_of(t));
+    s_cur = s_next;
   }
-  if (t_full < t_end) {
-    advance(t_full);
-    if (wave_active) tile(std::true_type{}, t_full, (t_full - t_begin) % NS);
-  }
+  // Only the last tile of the key range can run past the end of the sequence.
+  if (t_end * BN > n_keys)
+    softmax_pv(std::true_type{}, s_cur, t_end - 1, slot_of(t_end - 1));
+  else
+    softmax_pv(std::false_type{}, s_cur, t_end - 1, slot_of(t_end - 1));
 
   if (!wave_active) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);

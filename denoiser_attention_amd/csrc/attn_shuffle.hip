@@ -204,7 +204,11 @@ __global__ __launch_bounds__(64) void attn_shuffle_kernel(AttnParams p, int row_
 }
 
 // Merge split-KV partials: out = sum_s 2^(lse_s - lse) * O_s with
-// lse = log2 sum_s 2^lse_s.  One thread per (row, 4 columns).
+// lse = log2 sum_s 2^lse_s.  One thread per (row, 4 columns).  Loads are
+// issued in batches of kMergeBatch independent splits so that their latencies
+// overlap; the merge is an online (running max) combination in split order.
+constexpr int kMergeBatch = 8;
+
 template <typename TO>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const size_t rows = (size_t)p.B * p.Hq * p.L;
@@ -213,16 +217,30 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   if (gid >= rows * groups) return;
   const size_t row = gid / groups;
   const int g = (int)(gid % groups);
-  float mx = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, p.part_lse[(size_t)s * rows + row]);
+  float m = -INFINITY, wsum = 0.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.0f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float w = __builtin_amdgcn_exp2f(p.part_lse[(size_t)s * rows + row] - mx);
-    const f32x4 o = *reinterpret_cast<const f32x4*>(p.part_o + ((size_t)s * rows + row) * p.D +
-                                                    4 * g);
-    wsum += w;
-    acc += w * o;
+  for (int s0 = 0; s0 < p.splits; s0 += kMergeBatch) {
+    float lse[kMergeBatch];
+    f32x4 o[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (s0 + i < p.splits) {
+        const size_t r = (size_t)(s0 + i) * rows + row;
+        lse[i] = p.part_lse[r];
+        o[i] = *reinterpret_cast<const f32x4*>(p.part_o + r * p.D + 4 * g);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (s0 + i < p.splits) {
+        const float m_new = fmaxf(m, lse[i]);
+        const float a = __builtin_amdgcn_exp2f(m - m_new);       // 0 on the first split
+        const float w = __builtin_amdgcn_exp2f(lse[i] - m_new);
+        wsum = wsum * a + w;
+        acc = acc * a + w * o[i];
+        m = m_new;
+      }
+    }
   }
   const float inv = 1.0f / wsum;
   const size_t base = row * p.D + 4 * g;
