@@ -43,7 +43,24 @@ def parse_args():
     ap.add_argument("--prefix-len", type=int, default=None)
     ap.add_argument("--rotate", type=int, default=0, help="input sets rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of known size (1 GiB read + 1 GiB written),
+    repeated 4 times.  rocprofv3 FETCH_SIZE / WRITE_SIZE read on this kernel
+    give the scale factor from counter units to bytes."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": 4}}))
 
 
 def kernel_source_digest() -> str:
@@ -103,6 +120,10 @@ def main():
               "denoising step shards over sequences with no exchange, so throughput at N GPUs "
               "is N independent copies of this measurement.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 

@@ -17,7 +17,7 @@
 // topk_commit_kernel -- one workgroup per sequence: merges the chunk triples of
 //   each masked position in chunk order, forms the confidence, ranks every
 //   masked position by counting the masked positions ahead of it in the order
-//   (confidence descending, position ascending), 4 confidences per LDS read,
+//   (confidence descending, position ascending), 16 confidences per step,
 //   and commits rank < k.
 #include <climits>
 
@@ -145,19 +145,19 @@ __global__ __launch_bounds__(kThreads) void vocab_reduce_kernel(UnmaskParams p) 
 __global__ __launch_bounds__(kThreads) void topk_commit_kernel(UnmaskParams p) {
   // Confidences of the sequence; positions that are not masked hold -2, which
   // never compares >= a real confidence (those lie in (0, 1]).  The array is
-  // padded to a multiple of 4 so that the rank loop reads 16 bytes at a time.
+  // padded with -2 to a multiple of 16 for the rank loop.
   __shared__ __attribute__((aligned(16))) float s_conf[kUnmaskMaxL];
   __shared__ int s_pred[kUnmaskMaxL];
 
   const int b = blockIdx.x;
   const int L = p.L;
-  const int L4 = (L + 3) >> 2;
+  const int L16 = (L + 15) >> 4;
   const int tid = threadIdx.x;
   const size_t row0 = (size_t)b * L;
 
   // Every mask flag of the sequence is read before any is written, so
   // mask_out may alias mask_state.
-  for (int l = tid; l < 4 * L4; l += kThreads) {
+  for (int l = tid; l < 16 * L16; l += kThreads) {
     float conf = -2.0f;
     int pred = -1;
     if (l < L && p.mask_state[row0 + l] != 0) {
@@ -182,7 +182,8 @@ __global__ __launch_bounds__(kThreads) void topk_commit_kernel(UnmaskParams p) {
   __syncthreads();
 
   // rank(l) = #{masked j : conf_j > conf_l, or conf_j == conf_l and j < l};
-  // commit when rank < k.
+  // commit when rank < k.  Every lane reads the same LDS words (broadcast),
+  // 16 confidences per iteration from four independent 16-byte reads.
   const f32x4* c4 = reinterpret_cast<const f32x4*>(s_conf);
   for (int l = tid; l < L; l += kThreads) {
     const size_t row = row0 + l;
@@ -190,14 +191,17 @@ __global__ __launch_bounds__(kThreads) void topk_commit_kernel(UnmaskParams p) {
     const bool masked = c > -1.0f;
     int ahead = 0;
     if (masked && p.k > 0) {
-#pragma unroll 4
-      for (int j4 = 0; j4 < L4; ++j4) {
-        const f32x4 v = c4[j4];
-        const int j = 4 * j4;
-        ahead += (v.x > c || (v.x == c && j + 0 < l)) ? 1 : 0;
-        ahead += (v.y > c || (v.y == c && j + 1 < l)) ? 1 : 0;
-        ahead += (v.z > c || (v.z == c && j + 2 < l)) ? 1 : 0;
-        ahead += (v.w > c || (v.w == c && j + 3 < l)) ? 1 : 0;
+      for (int j16 = 0; j16 < L16; ++j16) {
+        f32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = c4[4 * j16 + u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 16 * j16 + 4 * u + e;
+            ahead += (v[u][e] > c || (v[u][e] == c && j < l)) ? 1 : 0;
+          }
       }
     }
     const bool commit = masked && ahead < p.k;
