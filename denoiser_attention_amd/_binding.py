@@ -31,7 +31,7 @@ class TTError(RuntimeError):
 
 
 class AttnOpts(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int), ("kv_splits", ctypes.c_int)]
+    _fields_ = [("path", ctypes.c_int), ("kv_splits", ctypes.c_int), ("kv_groups", ctypes.c_int)]
 
 
 _lib = None
@@ -113,8 +113,9 @@ def _cuda_contig(name: str, t: torch.Tensor, device: torch.device) -> None:
 
 
 def attn_workspace_bytes(batch, prefix_len, block_len, n_q_heads, n_kv_heads, head_dim,
-                         dtype: torch.dtype, path: str = "auto", kv_splits: int = 0) -> int:
-    opts = AttnOpts(_PATHS[path], kv_splits)
+                         dtype: torch.dtype, path: str = "auto", kv_splits: int = 0,
+                         kv_groups: int = 0) -> int:
+    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups)
     n = lib().tt_block_attn_workspace_bytes(batch, prefix_len, block_len, n_q_heads, n_kv_heads,
                                             head_dim, _dtype_code(dtype), ctypes.byref(opts))
     if n == SIZE_MAX:
@@ -123,7 +124,8 @@ def attn_workspace_bytes(batch, prefix_len, block_len, n_q_heads, n_kv_heads, he
 
 
 def block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, *, out=None, out_dtype=None,
-               path: str = "auto", kv_splits: int = 0, workspace=None, stream=None):
+               path: str = "auto", kv_splits: int = 0, kv_groups: int = 0, workspace=None,
+               stream=None):
     """Eq. (1) block attention through tt_block_attn_ex; returns ``out``.
 
     q [B,Hq,L,D]; k_ctx/v_ctx [B,Hkv,Pcap,D] (or None when prefix_len == 0);
@@ -156,8 +158,8 @@ def block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, *, out=None, ou
         out = torch.empty((B, Hq, L, D), dtype=out_dtype, device=device)
     _cuda_contig("out", out, device)
     _require(tuple(out.shape) == (B, Hq, L, D), "out must be [B, Hq, L, D]")
-    opts = AttnOpts(_PATHS[path], kv_splits)
-    need = attn_workspace_bytes(B, prefix_len, L, Hq, Hkv, D, q.dtype, path, kv_splits)
+    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups)
+    need = attn_workspace_bytes(B, prefix_len, L, Hq, Hkv, D, q.dtype, path, kv_splits, kv_groups)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -247,19 +249,20 @@ class Prepared:
 
 
 def prepare_block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, out, *,
-                       path: str = "auto", kv_splits: int = 0, workspace=None, stream=None):
+                       path: str = "auto", kv_splits: int = 0, kv_groups: int = 0,
+                       workspace=None, stream=None):
     """Validate once (same checks as block_attn) and return a Prepared call."""
     device = q.device
     B, Hq, L, D = q.shape
     Hkv = k_blk.shape[1]
     Pcap = 0 if k_ctx is None else k_ctx.shape[2]
-    need = attn_workspace_bytes(B, prefix_len, L, Hq, Hkv, D, q.dtype, path, kv_splits)
+    need = attn_workspace_bytes(B, prefix_len, L, Hq, Hkv, D, q.dtype, path, kv_splits, kv_groups)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
     # one validating call through the checked path
     block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, out=out, path=path,
-               kv_splits=kv_splits, workspace=workspace, stream=stream)
-    opts = AttnOpts(_PATHS[path], kv_splits)
+               kv_splits=kv_splits, kv_groups=kv_groups, workspace=workspace, stream=stream)
+    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups)
     ws_bytes = 0 if workspace is None else workspace.numel()
     args = (_ptr(q), _ptr(k_ctx), _ptr(v_ctx), prefix_len, _ptr(k_blk), _ptr(v_blk), L, Hq, Hkv,
             D, float(scale), _ptr(out), B, Pcap, _dtype_code(q.dtype), _dtype_code(out.dtype),

@@ -141,15 +141,24 @@ __device__ __forceinline__ void wait_tiles(int n_after) {
   }
 }
 
-template <int D, int NS, bool OUT_BF16, bool POS_SCALE>
-__global__ __launch_bounds__(kThreads, 2)
+// KG = 1: a workgroup is one group of 4 waves (128 query rows) streaming the
+// workgroup's key range.  KG = 2: two such groups share the same 128 rows and
+// split the key range between them (group 0 the leading floor(n/2) tiles,
+// group 1 the trailing ceil(n/2)), each with its own LDS ring; their partial
+// softmax states are merged through LDS at the end.  KG = 2 supplies key-range
+// parallelism without writing split partials to memory.
+template <int D, int NS, int KG, bool OUT_BF16, bool POS_SCALE>
+__global__ __launch_bounds__(kThreads * KG, 2 / KG)
 void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   using L = Lay<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[NS * L::STAGE_B];
+  __shared__ __attribute__((aligned(1024))) char smem_all[KG * NS * L::STAGE_B];
 
-  const int tid = threadIdx.x;
+  const int gtid = threadIdx.x;
+  const int kgrp = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane(gtid >> 8);  // key group
+  const int tid = gtid & (kThreads - 1);                    // thread index within the group
+  char* const smem = smem_all + kgrp * NS * L::STAGE_B;     // this group's ring
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave within the group
   const int lr = lane & 31, hh = lane >> 5;     // MFMA row/column lane, lane half
   const int grp = lane >> 4, gi = lane & 15;    // 16-lane group, index in group
 
@@ -162,8 +171,14 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
 
   const int n_keys = p.n_keys, P = p.P;
   const int n_tiles = (n_keys + BN - 1) / BN;
-  const int t_begin = split * p.tiles_per_split;
-  const int t_end = min(n_tiles, t_begin + p.tiles_per_split);
+  const int wg_begin = split * p.tiles_per_split;
+  const int wg_end = min(n_tiles, wg_begin + p.tiles_per_split);
+  const int wg_n = wg_end - wg_begin;
+  const int n_lead = KG == 1 ? 0 : wg_n / 2;        // tiles of group 0 when KG == 2
+  const int t_begin = kgrp == 0 ? wg_begin : wg_begin + n_lead;
+  const int t_end = KG == 1 ? wg_end : (kgrp == 0 ? wg_begin + n_lead : wg_end);
+  const int cnt = t_end - t_begin;                  // this group's tiles (may be 0)
+  const int nit = wg_n - n_lead;                    // iterations, equal for every group
 
   const char* kc = static_cast<const char*>(p.k_ctx) + (size_t)pair * p.Pcap * L::ROWB;
   const char* vc = static_cast<const char*>(p.v_ctx) + (size_t)pair * p.Pcap * L::ROWB;
@@ -187,10 +202,6 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
       const u32x4 v = row_ok ? src[2 * s + hh] : u32x4{0, 0, 0, 0};
       qf[s] = __builtin_bit_cast(bf16x8, v);
     }
-    // Consume Q here so that its load wait is placed before the K/V stream
-    // starts (and not inside the pipelined loop).
-#pragma unroll
-    for (int s = 0; s < L::DS; ++s) consume(qf[s]);
   }
 
   // LDS byte address of the ring.
@@ -352,37 +363,84 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // the slot of tile t-1, which every wave has finished with once it passes
   // the barrier of iteration t.
   static_assert((NS & (NS - 1)) == 0, "ring depth must be a power of two");
-  auto slot_of = [&](int u) { return (u - t_begin) & (NS - 1); };
-  // Wait until tile u has landed for the whole workgroup, then refill the slot
-  // of tile u-2 with tile u+NS-2.
-  auto advance = [&](int u) {
-    wait_tiles<D, NS>(min(NS - 3, t_end - 1 - u));
+  // Iteration index i of a group refers to its tile t_begin + i.
+  auto slot_of = [&](int i) { return i & (NS - 1); };
+  // Wait until the group's tile i has landed for every wave, then refill the
+  // slot of tile i-2 with tile i+NS-2.  Every wave of the workgroup runs the
+  // same number of these (and so of barriers), also past the end of its
+  // group's tiles.
+  auto advance = [&](int i) {
+    wait_tiles<D, NS>(max(0, min(NS - 3, cnt - 1 - i)));
     barrier();
-    if (u + NS - 2 < t_end) issue(u + NS - 2, slot_of(u + NS - 2));
+    if (i + NS - 2 < cnt) issue(t_begin + i + NS - 2, slot_of(i + NS - 2));
   };
 #pragma unroll
   for (int s = 0; s < NS - 2; ++s)
-    if (t_begin + s < t_end) issue(t_begin + s, s);
+    if (s < cnt) issue(t_begin + s, s);
+  // The Q loads (issued first) and the first K/V tiles are now all in flight.
+  // Consuming Q here makes its (conservative, full) load wait overlap the K/V
+  // latency and keeps it out of the pipelined loop.
+#pragma unroll
+  for (int s = 0; s < L::DS; ++s) consume(qf[s]);
   // Waves whose rows all lie past M run the same instruction stream on zero Q
   // rows (no branch in the loop) and store nothing.
-  advance(t_begin);
-  f32x16 s_cur = qk(slot_of(t_begin));
-#pragma unroll 2
-  for (int t = t_begin; t + 1 < t_end; ++t) {
-    advance(t + 1);
-    const f32x16 s_next = qk(slot_of(t + 1));
-    softmax_pv(std::false_type{}, s_cur, t, slot_of(t));
+  advance(0);
+  f32x16 s_cur = cnt > 0 ? qk(slot_of(0)) : f32x16{};
+  // Steady state: both groups have tiles i and i+1 (group 0 has at least
+  // nit - 1 tiles).
+  for (int i = 0; i + 2 < nit; ++i) {
+    advance(i + 1);
+    const f32x16 s_next = qk(slot_of(i + 1));
+    softmax_pv(std::false_type{}, s_cur, t_begin + i, slot_of(i));
     s_cur = s_next;
   }
-  // Only the last tile of the key range can run past the end of the sequence.
-  if (t_end * BN > n_keys)
-    softmax_pv(std::true_type{}, s_cur, t_end - 1, slot_of(t_end - 1));
-  else
-    softmax_pv(std::false_type{}, s_cur, t_end - 1, slot_of(t_end - 1));
+  if (nit >= 2) {   // last iteration of the loop, peeled: group 0 may lack tile nit-1
+    advance(nit - 1);
+    const f32x16 s_next = nit - 1 < cnt ? qk(slot_of(nit - 1)) : f32x16{};
+    softmax_pv(std::false_type{}, s_cur, t_begin + nit - 2, slot_of(nit - 2));
+    s_cur = s_next;
+  }
+  // Only the last tile of the whole key sequence can run past its end; it is
+  // always the group's tile nit-1.
+  if (nit - 1 < cnt) {
+    if (t_end * BN > n_keys)
+      softmax_pv(std::true_type{}, s_cur, t_begin + nit - 1, slot_of(nit - 1));
+    else
+      softmax_pv(std::false_type{}, s_cur, t_begin + nit - 1, slot_of(nit - 1));
+  }
 
-  if (!wave_active) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!row_ok) return;
+  float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (KG == 2) {
+    // Merge group 1's (max, sum, O) into group 0 through LDS (the rings are
+    // free once every wave is past its last tile).  Lanes of the two groups
+    // with the same (wave, lane) hold the same row and columns.
+    float* xbuf = reinterpret_cast<float*>(smem_all) + wave * (L::DB * 16 + 2) * 64;
+    barrier();
+    if (kgrp == 1) {
+#pragma unroll
+      for (int db = 0; db < L::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xbuf[(db * 16 + r) * 64 + lane] = oacc[db][r];
+      xbuf[(L::DB * 16) * 64 + lane] = m_run;
+      xbuf[(L::DB * 16 + 1) * 64 + lane] = l_tot;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    barrier();
+    if (kgrp == 1) return;
+    const float m1 = xbuf[(L::DB * 16) * 64 + lane];
+    const float l1 = xbuf[(L::DB * 16 + 1) * 64 + lane];
+    const float m_new = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 for an empty group
+    const float a1 = __builtin_amdgcn_exp2f(m1 - m_new);
+#pragma unroll
+    for (int db = 0; db < L::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        oacc[db][r] = oacc[db][r] * a0 + xbuf[(db * 16 + r) * 64 + lane] * a1;
+    l_tot = l_tot * a0 + l1 * a1;
+    m_run = m_new;
+  }
+  if (!wave_active || !row_ok) return;
   const size_t grow = row_base + r_local;
   const float inv = 1.0f / l_tot;
   if (p.splits == 1) {
@@ -428,8 +486,12 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   const int m_tiles = (p.M + BM - 1) / BM;
   const long long n = (long long)m_tiles * p.splits * p.B * p.Hkv;
   if (n <= 0 || n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, OUT_BF16, POS>), dim3((unsigned)n),
-                     dim3(kThreads), 0, stream, p, m_tiles, (int)n);
+  if (p.kgroups == 2)
+    hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 2, OUT_BF16, POS>), dim3((unsigned)n),
+                       dim3(2 * kThreads), 0, stream, p, m_tiles, (int)n);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, OUT_BF16, POS>), dim3((unsigned)n),
+                       dim3(kThreads), 0, stream, p, m_tiles, (int)n);
   return hipGetLastError();
 }
 

@@ -39,6 +39,7 @@ tt_status device_present() {
 
 struct AttnPlan {
   int path = TT_ATTN_SHUFFLE;  // resolved family
+  int kgroups = 1;             // MFMA: wave groups splitting a workgroup's keys
   int splits = 1;
   int tiles_per_split = 1;
   bool empty = false;          // nothing to compute
@@ -57,6 +58,7 @@ tt_status plan_attn(int B, int P, int L, int Hq, int Hkv, int D, tt_dtype dtype,
   const int req = opts ? opts->path : TT_ATTN_AUTO;
   if (req != TT_ATTN_AUTO && req != TT_ATTN_MFMA && req != TT_ATTN_SHUFFLE) return TT_EINVAL;
   if (opts && opts->kv_splits < 0) return TT_EINVAL;
+  if (opts && (opts->kv_groups < 0 || opts->kv_groups > 2)) return TT_EINVAL;
   if ((long long)P + L > INT_MAX / 2) return TT_EUNSUPPORTED;
   const int G = Hq / Hkv;
   const long long M = (long long)G * L;
@@ -86,28 +88,41 @@ tt_status plan_attn(int B, int P, int L, int Hq, int Hkv, int D, tt_dtype dtype,
   }
 
   const long long n_keys = (long long)P + L;
-  long long n_tiles, base, target;
+  long long n_tiles, splits;
   if (plan->path == TT_ATTN_MFMA) {
+    // Units of 4 waves x 128 query rows; 512 of them fill 256 CUs at 2 waves
+    // per SIMD.  With fewer query tiles than that, two wave groups per
+    // workgroup split each workgroup's key range on chip, and workgroups split
+    // it further (with a merge pass) only as far as still needed.
     n_tiles = cdiv(n_keys, tt::kAttnMfmaBN);
-    base = cdiv(M, tt::kAttnMfmaBM) * B * Hkv;
-    target = kMfmaTargetWG;
+    const long long base = cdiv(M, tt::kAttnMfmaBM) * B * Hkv;
+    const int req_groups = opts ? opts->kv_groups : 0;
+    plan->kgroups = req_groups ? req_groups : (base >= kMfmaTargetWG ? 1 : 2);
+    if (opts && opts->kv_splits > 0) {
+      splits = opts->kv_splits < n_tiles ? opts->kv_splits : n_tiles;
+    } else {
+      splits = cdiv(kMfmaTargetWG / plan->kgroups, base);
+      const long long min_tiles = 2 * plan->kgroups;   // per workgroup
+      const long long max_splits = n_tiles / min_tiles > 1 ? n_tiles / min_tiles : 1;
+      if (splits > max_splits) splits = max_splits;
+      if (splits < 1) splits = 1;
+    }
+    if (base * splits > INT_MAX) return TT_EUNSUPPORTED;
   } else {
     n_tiles = cdiv(n_keys, tt::kAttnShufBN);
-    base = cdiv(M, tt::kAttnShufRows) * B * Hkv;
-    target = kShufTargetWG;
-  }
-  long long splits;
-  if (opts && opts->kv_splits > 0) {
-    splits = opts->kv_splits < n_tiles ? opts->kv_splits : n_tiles;
-  } else {
-    splits = cdiv(target, base);
-    const long long max_splits = n_tiles / 2 > 1 ? n_tiles / 2 : 1;
-    if (splits > max_splits) splits = max_splits;
-    if (splits < 1) splits = 1;
+    const long long base = cdiv(M, tt::kAttnShufRows) * B * Hkv;
+    if (opts && opts->kv_splits > 0) {
+      splits = opts->kv_splits < n_tiles ? opts->kv_splits : n_tiles;
+    } else {
+      splits = cdiv(kShufTargetWG, base);
+      const long long max_splits = n_tiles / 2 > 1 ? n_tiles / 2 : 1;
+      if (splits > max_splits) splits = max_splits;
+      if (splits < 1) splits = 1;
+    }
+    if (base * splits > INT_MAX) return TT_EUNSUPPORTED;
   }
   const long long tps = cdiv(n_tiles, splits);
   splits = cdiv(n_tiles, tps);   // no empty split
-  if (base * splits > INT_MAX) return TT_EUNSUPPORTED;
   plan->splits = (int)splits;
   plan->tiles_per_split = (int)tps;
   if (splits > 1) {
@@ -206,6 +221,7 @@ TT_EXPORT tt_status tt_block_attn_ex(const void* q, const void* k_ctx, const voi
   p.n_keys = prefix_len + block_len;
   p.splits = plan.splits;
   p.tiles_per_split = plan.tiles_per_split;
+  p.kgroups = plan.kgroups;
   p.out_bf16 = out_dtype == TT_BF16 ? 1 : 0;
   p.scale_log2 = scale * kLog2e;
   if (plan.splits > 1) {

@@ -20,8 +20,9 @@ struct AttnParams {
   int B, Hq, Hkv, G, L, P, Pcap, D;
   int M;               // G*L packed query rows per (batch, kv head)
   int n_keys;          // P + L
-  int splits;          // key-range splits per query tile (>= 1)
+  int splits;          // key-range splits per query tile (>= 1), one workgroup each
   int tiles_per_split; // key tiles handled by one split
+  int kgroups;         // MFMA kernel: 1 or 2 key groups inside a workgroup
   int out_bf16;        // 1: write bf16 output, 0: fp32
   float scale_log2;    // softmax scale * log2(e)
 };

@@ -61,10 +61,14 @@ typedef enum { TT_ATTN_AUTO = 0, TT_ATTN_MFMA = 1, TT_ATTN_SHUFFLE = 2 } tt_attn
 
 /* Optional tuning knobs of tt_block_attn_ex.  kv_splits = 0 lets the library
  * choose how many workgroups share one query tile's key range; a positive value
- * forces that many (clamped so that no split is empty). */
+ * forces that many (clamped so that no split is empty; partial results are then
+ * merged in a second pass).  kv_groups (MFMA kernel only) = 0 lets the library
+ * choose, 1 or 2 forces how many wave groups inside one workgroup divide that
+ * workgroup's key range between them (merged on chip). */
 typedef struct {
   int path;       /* tt_attn_path */
   int kv_splits;  /* 0 = auto */
+  int kv_groups;  /* 0 = auto, 1 or 2 */
 } tt_attn_opts;
 
 /* Human-readable name of a status code (static storage, never NULL). */

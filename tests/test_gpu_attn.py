@@ -67,6 +67,19 @@ def test_bf16_forced_splits(splits):
     check_attn(got, oracle_attn(inp), "bf16", True, f"splits={splits}")
 
 
+# Key-tile counts 1, 2, 3, 5 and 7 (32-key tiles), forced one or two wave groups
+# per workgroup, with and without extra workgroup splits.
+@pytest.mark.parametrize("n_keys", [20, 64, 65, 150, 223])
+@pytest.mark.parametrize("groups,splits", [(1, 0), (2, 0), (2, 2), (1, 3)])
+def test_bf16_key_groups(n_keys, groups, splits):
+    L = 9
+    cfg = small_cfg(batch=2, n_q_heads=16, n_kv_heads=2, prefix_len=n_keys - L, block_len=L)
+    inp = synth.attn_inputs(cfg, seed=7, prefix_cap=n_keys - L + 3)
+    got = gpu_attn(inp, DEV, path="mfma", kv_groups=groups, kv_splits=splits,
+                   out_dtype=torch.float32)
+    check_attn(got, oracle_attn(inp), "bf16", False, f"keys={n_keys} groups={groups} splits={splits}")
+
+
 def test_paths_agree_and_deterministic():
     cfg = small_cfg(batch=2, prefix_len=257, block_len=32)
     inp = synth.attn_inputs(cfg, seed=4)
