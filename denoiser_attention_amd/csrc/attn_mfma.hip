@@ -410,6 +410,12 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   }
 
   float l_tot = l_run + __shfl_xor(l_run, 32);
+  // Staging tile for the output: each wave writes its normalised 32 x D block
+  // to LDS (fp32, 16-byte chunk c of row r at chunk position c ^ (r & 7), so
+  // that both the accumulator-order writes and the row-order reads spread over
+  // all banks) and reads it back row by row, so that the global stores cover
+  // whole contiguous rows.
+  float* stg;
   if (KG == 2) {
     // Merge group 1's (max, sum, O) into group 0 through LDS (the rings are
     // free once every wave is past its last tile).  Lanes of the two groups
@@ -439,43 +445,60 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
         oacc[db][r] = oacc[db][r] * a0 + xbuf[(db * 16 + r) * 64 + lane] * a1;
     l_tot = l_tot * a0 + l1 * a1;
     m_run = m_new;
-  }
-  if (!wave_active || !row_ok) return;
-  const size_t grow = row_base + r_local;
-  const float inv = 1.0f / l_tot;
-  if (p.splits == 1) {
-#pragma unroll
-    for (int db = 0; db < L::DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = db * 32 + 8 * g + 4 * hh;
-        const float o0 = oacc[db][4 * g + 0] * inv, o1 = oacc[db][4 * g + 1] * inv;
-        const float o2 = oacc[db][4 * g + 2] * inv, o3 = oacc[db][4 * g + 3] * inv;
-        if (OUT_BF16) {
-          u32x2 pk;
-          pk.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o0) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o1) << 16);
-          pk.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o2) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o3) << 16);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + grow * D + col) = pk;
-        } else {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + grow * D + col) =
-              f32x4{o0, o1, o2, o3};
-        }
-      }
+    // This wave alone reads and then rewrites its own exchange area (LDS
+    // operations of one wave complete in order).
+    stg = xbuf;
   } else {
+    barrier();   // every wave is done with the ring
+    stg = reinterpret_cast<float*>(smem_all) + wave * 32 * D;
+  }
+  static_assert(32 * D <= (L::DB * 16 + 2) * 64, "staging tile fits the exchange area");
+  static_assert(kWaves * 32 * D * 4 <= NS * L::STAGE_B, "staging tiles fit the ring");
+  if (!wave_active) return;
+  const float inv = 1.0f / l_tot;
+#pragma unroll
+  for (int db = 0; db < L::DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int chunk = db * 8 + 2 * g + hh;
+      *reinterpret_cast<f32x4*>(stg + lr * D + ((chunk ^ (lr & 7)) << 2)) =
+          f32x4{oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
+                oacc[db][4 * g + 3] * inv};
+    }
+  asm volatile("" ::: "memory");
+  const int rows_here = min(32, p.M - wave_row0);   // valid rows of this wave
+  const size_t grow0 = row_base + wave_row0;
+  if (OUT_BF16) {
+    // 8 values (16 bytes) per lane, D/8 lanes per row.
+    constexpr int LPR = D / 8, RPI = 64 / LPR;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = i * RPI + lane / LPR, c8 = lane % LPR;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(stg + row * D + (((2 * c8) ^ (row & 7)) << 2));
+      const f32x4 bq = *reinterpret_cast<const f32x4*>(stg + row * D + (((2 * c8 + 1) ^ (row & 7)) << 2));
+      u32x4 pk;
+      pk.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a.x) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a.y) << 16);
+      pk.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a.z) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a.w) << 16);
+      pk.z = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.x) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.y) << 16);
+      pk.w = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.z) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.w) << 16);
+      if (row < rows_here)
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + (grow0 + row) * D + 8 * c8) = pk;
+    }
+  } else {
+    // 4 values (16 bytes) per lane, D/4 lanes per row: the final fp32 output,
+    // or this split's partial.
+    constexpr int LPR = D / 4, RPI = 64 / LPR;
     const size_t rows_total = (size_t)p.B * p.Hq * p.L;
-    float* po = p.part_o + ((size_t)split * rows_total + grow) * D;
+    float* dst = p.splits == 1 ? static_cast<float*>(p.out) + grow0 * D
+                               : p.part_o + ((size_t)split * rows_total + grow0) * D;
 #pragma unroll
-    for (int db = 0; db < L::DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = db * 32 + 8 * g + 4 * hh;
-        *reinterpret_cast<f32x4*>(po + col) =
-            f32x4{oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
-                  oacc[db][4 * g + 3] * inv};
-      }
-    if (hh == 0) p.part_lse[(size_t)split * rows_total + grow] = m_run + __log2f(l_tot);
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = i * RPI + lane / LPR, c4 = lane % LPR;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stg + row * D + ((c4 ^ (row & 7)) << 2));
+      if (row < rows_here) *reinterpret_cast<f32x4*>(dst + (size_t)row * D + 4 * c4) = v;
+    }
+    if (p.splits > 1 && hh == 0 && row_ok)
+      p.part_lse[(size_t)split * rows_total + row_base + r_local] = m_run + __log2f(l_tot);
   }
 }
 
