@@ -6,15 +6,18 @@ synthetic-input generator (``synth``).
 
     block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale)  -> out
     unmask_step(logits, mask_state, k, tokens)                     -> (tokens, mask_out)
+    unmask_step_ex(logits, mask_state, select_rule(...), tokens)   -> (tokens, mask_out)
 """
 from ._binding import (  # noqa: F401
-    LIB_PATH, Prepared, TTError, attn_workspace_bytes, block_attn, lib, prepare_block_attn,
-    prepare_unmask_commit, prepare_unmask_reduce, status_string, unmask_commit, unmask_reduce,
-    unmask_step, unmask_workspace_bytes, version,
+    LIB_PATH, SELECT_MODES, Prepared, Select, TTError, attn_workspace_bytes, block_attn, lib,
+    prepare_block_attn, prepare_unmask_commit, prepare_unmask_commit_ex, prepare_unmask_reduce,
+    select_rule, status_string, unmask_commit, unmask_commit_ex, unmask_reduce, unmask_step,
+    unmask_step_ex, unmask_workspace_bytes, version,
 )
 
 __all__ = [
-    "LIB_PATH", "Prepared", "TTError", "attn_workspace_bytes", "block_attn", "lib",
-    "prepare_block_attn", "prepare_unmask_commit", "prepare_unmask_reduce", "status_string",
-    "unmask_commit", "unmask_reduce", "unmask_step", "unmask_workspace_bytes", "version",
+    "LIB_PATH", "SELECT_MODES", "Prepared", "Select", "TTError", "attn_workspace_bytes",
+    "block_attn", "lib", "prepare_block_attn", "prepare_unmask_commit", "prepare_unmask_commit_ex",
+    "prepare_unmask_reduce", "select_rule", "status_string", "unmask_commit", "unmask_commit_ex",
+    "unmask_reduce", "unmask_step", "unmask_step_ex", "unmask_workspace_bytes", "version",
 ]

@@ -34,6 +34,24 @@ class AttnOpts(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("kv_splits", ctypes.c_int), ("kv_groups", ctypes.c_int)]
 
 
+class Select(ctypes.Structure):
+    """tt_select: the selection rule of one unmasking step."""
+    _fields_ = [("mode", ctypes.c_int), ("k", ctypes.c_int), ("gamma", ctypes.c_float),
+                ("steps_left", ctypes.c_int), ("step", ctypes.c_int), ("n_steps", ctypes.c_int)]
+
+
+SELECT_MODES = {"top_k": 0, "threshold": 1, "schedule": 2, "leftmost": 3}
+
+
+def select_rule(mode: str, *, k: int = 0, gamma: float = 0.0, steps_left: int = 1, step: int = 1,
+                n_steps: int = 1) -> Select:
+    """Build a tt_select: "top_k" (k), "threshold" (gamma, steps_left),
+    "schedule" (step, n_steps) or "leftmost" (k)."""
+    _require(mode in SELECT_MODES, f"unknown selection mode {mode!r}")
+    return Select(SELECT_MODES[mode], int(k), float(gamma), int(steps_left), int(step),
+                  int(n_steps))
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -50,6 +68,10 @@ _SIGNATURES = {
     "tt_unmask_step": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "tt_unmask_reduce": (_i, [_vp, _vp, _i, _i, _i, _vp, _sz, _vp]),
     "tt_unmask_commit": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "tt_unmask_step_ex": (_i, [_vp, _vp, ctypes.POINTER(Select), _vp, _vp, _i, _i, _i, _vp, _vp,
+                               _vp, _sz, _vp]),
+    "tt_unmask_commit_ex": (_i, [_vp, ctypes.POINTER(Select), _vp, _vp, _i, _i, _i, _vp, _vp, _vp,
+                                 _sz, _vp]),
 }
 
 
@@ -214,6 +236,25 @@ def unmask_step(logits, mask_state, k, tokens, *, mask_out=None, conf_out=None, 
     return tokens, mask_out
 
 
+def unmask_step_ex(logits, mask_state, select: Select, tokens, *, mask_out=None, conf_out=None,
+                   pred_out=None, workspace=None, stream=None):
+    """One unmask step under any selection rule (tt_unmask_step_ex)."""
+    device, B, L = _unmask_checks(logits, mask_state, tokens, mask_out, conf_out, pred_out)
+    V = logits.shape[2]
+    if mask_out is None:
+        mask_out = torch.empty_like(mask_state)
+    need = unmask_workspace_bytes(B, L, V)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib().tt_unmask_step_ex(_ptr(logits), _ptr(mask_state), ctypes.byref(select),
+                                 _ptr(tokens), _ptr(mask_out), B, L, V, _ptr(conf_out),
+                                 _ptr(pred_out), _ptr(workspace), ws_bytes,
+                                 _stream(device, stream))
+    _check(st, "tt_unmask_step_ex")
+    return tokens, mask_out
+
+
 def unmask_reduce(logits, mask_state, workspace, *, stream=None):
     """First half of tt_unmask_step (vocabulary pass into ``workspace``)."""
     device, B, L = _unmask_checks(logits, mask_state, None, None, None, None)
@@ -230,6 +271,16 @@ def unmask_commit(mask_state, k, tokens, mask_out, vocab, workspace, *, conf_out
                                 vocab, _ptr(conf_out), _ptr(pred_out), _ptr(workspace),
                                 workspace.numel(), _stream(device, stream))
     _check(st, "tt_unmask_commit")
+
+
+def unmask_commit_ex(mask_state, select: Select, tokens, mask_out, vocab, workspace, *,
+                     conf_out=None, pred_out=None, stream=None):
+    """Second half of tt_unmask_step_ex (merge, select, commit)."""
+    device, B, L = _unmask_checks(None, mask_state, tokens, mask_out, conf_out, pred_out)
+    st = lib().tt_unmask_commit_ex(_ptr(mask_state), ctypes.byref(select), _ptr(tokens),
+                                   _ptr(mask_out), B, L, vocab, _ptr(conf_out), _ptr(pred_out),
+                                   _ptr(workspace), workspace.numel(), _stream(device, stream))
+    _check(st, "tt_unmask_commit_ex")
 
 
 class Prepared:
@@ -289,3 +340,16 @@ def prepare_unmask_commit(mask_state, k, tokens, mask_out, vocab, workspace, *, 
             _ptr(pred_out), _ptr(workspace), workspace.numel(), _stream(device, stream))
     return Prepared(lib().tt_unmask_commit, args, "tt_unmask_commit",
                     (mask_state, tokens, mask_out, workspace, conf_out, pred_out))
+
+
+def prepare_unmask_commit_ex(mask_state, select: Select, tokens, mask_out, vocab, workspace, *,
+                             conf_out=None, pred_out=None, stream=None):
+    device, B, L = _unmask_checks(None, mask_state, tokens, mask_out, conf_out, pred_out)
+    _require(workspace.numel() >= unmask_workspace_bytes(B, L, vocab), "workspace too small")
+    sel = Select(select.mode, select.k, select.gamma, select.steps_left, select.step,
+                 select.n_steps)
+    args = (_ptr(mask_state), ctypes.byref(sel), _ptr(tokens), _ptr(mask_out), B, L, vocab,
+            _ptr(conf_out), _ptr(pred_out), _ptr(workspace), workspace.numel(),
+            _stream(device, stream))
+    return Prepared(lib().tt_unmask_commit_ex, args, "tt_unmask_commit_ex",
+                    (mask_state, tokens, mask_out, workspace, conf_out, pred_out, sel))

@@ -294,48 +294,96 @@ TT_EXPORT tt_status tt_unmask_reduce(const float* logits, const uint8_t* mask_st
   return to_status(tt::launch_vocab_reduce(p, stream));
 }
 
-TT_EXPORT tt_status tt_unmask_commit(const uint8_t* mask_state, int k, int32_t* tokens_out,
-                                     uint8_t* mask_out, int batch, int block_len, int vocab,
-                                     float* conf_out, int32_t* pred_out, const void* workspace,
-                                     size_t workspace_bytes, hipStream_t stream) {
-  if (k < 0) return TT_EINVAL;
-  UnmaskPlan plan;
+namespace {
+
+// Validates a selection rule and stores it in p.
+tt_status set_select(const tt_select* sel, UnmaskParams* p) {
+  if (!sel) return TT_EINVAL;
+  p->mode = sel->mode;
+  p->k = 0;
+  p->gamma = 0.0f;
+  p->steps_left = p->step = p->n_steps = 1;
+  switch (sel->mode) {
+    case TT_SELECT_TOP_K:
+    case TT_SELECT_LEFTMOST:
+      if (sel->k < 0) return TT_EINVAL;
+      p->k = sel->k;
+      return TT_OK;
+    case TT_SELECT_THRESHOLD:
+      if (!std::isfinite(sel->gamma) || sel->steps_left < 1) return TT_EINVAL;
+      p->gamma = sel->gamma;
+      p->steps_left = sel->steps_left;
+      return TT_OK;
+    case TT_SELECT_SCHEDULE:
+      if (sel->n_steps < 1 || sel->step < 1 || sel->step > sel->n_steps) return TT_EINVAL;
+      p->step = sel->step;
+      p->n_steps = sel->n_steps;
+      return TT_OK;
+    default:
+      return TT_EINVAL;
+  }
+}
+
+tt_status unmask_run(const float* logits, const uint8_t* mask_state, const tt_select* sel,
+                     int32_t* tokens_out, uint8_t* mask_out, int batch, int block_len, int vocab,
+                     float* conf_out, int32_t* pred_out, const void* workspace,
+                     size_t workspace_bytes, hipStream_t stream, bool reduce) {
   UnmaskParams p{};
-  tt_status st = unmask_prepare(nullptr, mask_state, batch, block_len, vocab, workspace,
-                                workspace_bytes, &plan, &p);
+  tt_status st = set_select(sel, &p);
+  if (st != TT_OK) return st;
+  UnmaskPlan plan;
+  st = unmask_prepare(logits, mask_state, batch, block_len, vocab, workspace, workspace_bytes,
+                      &plan, &p);
   if (st != TT_OK || plan.empty) return st;
-  if (!tokens_out || !mask_out) return TT_EINVAL;
+  if ((reduce && !logits) || !tokens_out || !mask_out) return TT_EINVAL;
   st = device_present();
   if (st != TT_OK) return st;
-  p.k = k;
   p.tokens_out = tokens_out;
   p.mask_out = mask_out;
   p.conf_out = conf_out;
   p.pred_out = pred_out;
   (void)hipGetLastError();
+  if (reduce) {
+    const hipError_t e = tt::launch_vocab_reduce(p, stream);
+    if (e != hipSuccess) return TT_EHIP;
+  }
   return to_status(tt::launch_topk_commit(p, stream));
+}
+
+}  // namespace
+
+TT_EXPORT tt_status tt_unmask_commit(const uint8_t* mask_state, int k, int32_t* tokens_out,
+                                     uint8_t* mask_out, int batch, int block_len, int vocab,
+                                     float* conf_out, int32_t* pred_out, const void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  tt_select sel{TT_SELECT_TOP_K, k, 0.0f, 1, 1, 1};
+  return unmask_run(nullptr, mask_state, &sel, tokens_out, mask_out, batch, block_len, vocab,
+                    conf_out, pred_out, workspace, workspace_bytes, stream, false);
+}
+
+TT_EXPORT tt_status tt_unmask_commit_ex(const uint8_t* mask_state, const tt_select* select,
+                                        int32_t* tokens_out, uint8_t* mask_out, int batch,
+                                        int block_len, int vocab, float* conf_out,
+                                        int32_t* pred_out, const void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  return unmask_run(nullptr, mask_state, select, tokens_out, mask_out, batch, block_len, vocab,
+                    conf_out, pred_out, workspace, workspace_bytes, stream, false);
 }
 
 TT_EXPORT tt_status tt_unmask_step(const float* logits, const uint8_t* mask_state, int k,
                                    int32_t* tokens_out, uint8_t* mask_out, int batch,
                                    int block_len, int vocab, float* conf_out, int32_t* pred_out,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (k < 0) return TT_EINVAL;
-  UnmaskPlan plan;
-  UnmaskParams p{};
-  tt_status st = unmask_prepare(logits, mask_state, batch, block_len, vocab, workspace,
-                                workspace_bytes, &plan, &p);
-  if (st != TT_OK || plan.empty) return st;
-  if (!logits || !tokens_out || !mask_out) return TT_EINVAL;
-  st = device_present();
-  if (st != TT_OK) return st;
-  p.k = k;
-  p.tokens_out = tokens_out;
-  p.mask_out = mask_out;
-  p.conf_out = conf_out;
-  p.pred_out = pred_out;
-  (void)hipGetLastError();
-  hipError_t e = tt::launch_vocab_reduce(p, stream);
-  if (e != hipSuccess) return TT_EHIP;
-  return to_status(tt::launch_topk_commit(p, stream));
+  tt_select sel{TT_SELECT_TOP_K, k, 0.0f, 1, 1, 1};
+  return unmask_run(logits, mask_state, &sel, tokens_out, mask_out, batch, block_len, vocab,
+                    conf_out, pred_out, workspace, workspace_bytes, stream, true);
+}
+
+TT_EXPORT tt_status tt_unmask_step_ex(const float* logits, const uint8_t* mask_state,
+                                      const tt_select* select, int32_t* tokens_out,
+                                      uint8_t* mask_out, int batch, int block_len, int vocab,
+                                      float* conf_out, int32_t* pred_out, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  return unmask_run(logits, mask_state, select, tokens_out, mask_out, batch, block_len, vocab,
+                    conf_out, pred_out, workspace, workspace_bytes, stream, true);
 }

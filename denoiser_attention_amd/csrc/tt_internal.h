@@ -59,7 +59,12 @@ struct UnmaskParams {
   int32_t* pred_out;        // optional
   VocabPartial* partials;   // [B*L, n_chunks]
   int B, L, V, k, n_chunks;
+  // Selection rule (values of tt_select_mode) and its parameters.
+  int mode;
+  float gamma;
+  int steps_left, step, n_steps;
 };
+enum { kSelTopK = 0, kSelThreshold = 1, kSelSchedule = 2, kSelLeftmost = 3 };
 
 hipError_t launch_vocab_reduce(const UnmaskParams& p, hipStream_t stream);
 hipError_t launch_topk_commit(const UnmaskParams& p, hipStream_t stream);

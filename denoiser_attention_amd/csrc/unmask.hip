@@ -17,8 +17,10 @@
 // topk_commit_kernel -- one workgroup per sequence: merges the chunk triples of
 //   each masked position in chunk order, forms the confidence, ranks every
 //   masked position by counting the masked positions ahead of it in the order
-//   (confidence descending, position ascending), 16 confidences per step,
-//   and commits rank < k.
+//   (confidence descending, position ascending; position ascending alone for
+//   the mock-autoregressive rule), 16 confidences per step, and commits
+//   rank < k, where k comes from the selection rule: fixed, or derived from
+//   the sequence's masked count and its count of confidences above gamma.
 #include <climits>
 
 #include "tt_internal.h"
@@ -155,6 +157,11 @@ __global__ __launch_bounds__(kThreads) void topk_commit_kernel(UnmaskParams p) {
   const int tid = threadIdx.x;
   const size_t row0 = (size_t)b * L;
 
+  __shared__ int s_count[2];   // masked positions, masked positions with conf > gamma
+  if (tid < 2) s_count[tid] = 0;
+  __syncthreads();
+  int my_masked = 0, my_above = 0;
+
   // Every mask flag of the sequence is read before any is written, so
   // mask_out may alias mask_state.
   for (int l = tid; l < 16 * L16; l += kThreads) {
@@ -175,11 +182,28 @@ __global__ __launch_bounds__(kThreads) void topk_commit_kernel(UnmaskParams p) {
       }
       conf = 1.0f / t.s;
       pred = t.arg;
+      ++my_masked;
+      my_above += conf > p.gamma ? 1 : 0;
     }
     s_conf[l] = conf;
     if (l < L) s_pred[l] = pred;
   }
+  if (p.mode == kSelThreshold || p.mode == kSelSchedule) {
+    if (my_masked) atomicAdd(&s_count[0], my_masked);
+    if (my_above) atomicAdd(&s_count[1], my_above);
+  }
   __syncthreads();
+
+  // Number of positions this sequence commits.
+  int k = p.k;
+  if (p.mode == kSelThreshold) {
+    const int n = s_count[0];
+    k = min(n, max(s_count[1], (n + p.steps_left - 1) / p.steps_left));
+  } else if (p.mode == kSelSchedule) {
+    const long long keep = (long long)L * (p.n_steps - p.step) / p.n_steps;
+    k = (int)max(0LL, (long long)s_count[0] - keep);
+  }
+  const bool leftmost = p.mode == kSelLeftmost;
 
   // rank(l) = #{masked j : conf_j > conf_l, or conf_j == conf_l and j < l};
   // commit when rank < k.  Every lane reads the same LDS words (broadcast),
@@ -190,7 +214,10 @@ __global__ __launch_bounds__(kThreads) void topk_commit_kernel(UnmaskParams p) {
     const float c = s_conf[l];
     const bool masked = c > -1.0f;
     int ahead = 0;
-    if (masked && p.k > 0) {
+    if (masked && k > 0 && leftmost) {
+      // Masked positions before l.
+      for (int j = 0; j < l; ++j) ahead += s_conf[j] > -1.0f ? 1 : 0;
+    } else if (masked && k > 0) {
       for (int j16 = 0; j16 < L16; ++j16) {
         f32x4 v[4];
 #pragma unroll
@@ -204,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void topk_commit_kernel(UnmaskParams p) {
           }
       }
     }
-    const bool commit = masked && ahead < p.k;
+    const bool commit = masked && ahead < k;
     if (commit) p.tokens_out[row] = s_pred[l];
     p.mask_out[row] = (masked && !commit) ? 1 : 0;
     if (p.conf_out) p.conf_out[row] = masked ? c : -1.0f;

@@ -175,6 +175,62 @@ tt_status tt_unmask_commit(const uint8_t* mask_state, int k, int32_t* tokens_out
                            float* conf_out, int32_t* pred_out, const void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* Selection rule of one unmasking step: TwoTower paper §2.2 "Sampling" and
+ * Algorithm 2, plus the one-token-per-step mode named in the "Versatile
+ * Operation: Three Generation Modes" list of the article "NVIDIA's
+ * Nemotron-Labs-TwoTower: Boosting AI Text Generation Speed".  Every rule
+ * ranks the still-masked positions of a sequence and commits a prefix of that
+ * ranking; n is the number of masked positions of the sequence.
+ *   TT_SELECT_TOP_K      ranking (conf descending, position ascending);
+ *                        commits min(k, n).  Same as tt_unmask_step.
+ *   TT_SELECT_THRESHOLD  Algorithm 2's ConfidenceSample with threshold gamma and
+ *                        steps_left = T - r + 1 remaining steps: every position
+ *                        with conf > gamma (strict, in fp32), and at least
+ *                        ceil(n / steps_left) of them, i.e. the first
+ *                        min(n, max(#{conf > gamma}, ceil(n / steps_left))) of
+ *                        the same ranking.  n masked positions are therefore
+ *                        gone after steps_left steps; steps_left == 1 commits all.
+ *   TT_SELECT_SCHEDULE   predict-and-noise with the linear schedule
+ *                        alpha_t = 1 - t: step `step` (1-based) of `n_steps`
+ *                        leaves floor(block_len * (n_steps - step) / n_steps)
+ *                        positions masked and re-masks the least confident
+ *                        predictions, i.e. commits the first
+ *                        max(0, n - floor(block_len * (n_steps - step) / n_steps))
+ *                        of the same ranking.
+ *   TT_SELECT_LEFTMOST   mock-autoregressive: commits the min(k, n) masked
+ *                        positions of lowest index, whatever their confidence
+ *                        (k = 1: one token per step, left to right).
+ * Fields a rule does not use are ignored. */
+typedef enum {
+  TT_SELECT_TOP_K = 0,
+  TT_SELECT_THRESHOLD = 1,
+  TT_SELECT_SCHEDULE = 2,
+  TT_SELECT_LEFTMOST = 3
+} tt_select_mode;
+
+typedef struct {
+  int mode;        /* tt_select_mode */
+  int k;           /* TOP_K, LEFTMOST: >= 0 */
+  float gamma;     /* THRESHOLD: finite */
+  int steps_left;  /* THRESHOLD: >= 1 */
+  int step;        /* SCHEDULE: 1 <= step <= n_steps */
+  int n_steps;     /* SCHEDULE: >= 1 */
+} tt_select;
+
+/* tt_unmask_step / tt_unmask_commit under any selection rule.  `select` must
+ * not be NULL; an unknown mode or a field outside its range returns TT_EINVAL.
+ * All other arguments, outputs and guarantees are those of tt_unmask_step
+ * (conf_out and pred_out report every masked position, committed or not). */
+tt_status tt_unmask_step_ex(const float* logits, const uint8_t* mask_state,
+                            const tt_select* select, int32_t* tokens_out, uint8_t* mask_out,
+                            int batch, int block_len, int vocab, float* conf_out,
+                            int32_t* pred_out, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+tt_status tt_unmask_commit_ex(const uint8_t* mask_state, const tt_select* select,
+                              int32_t* tokens_out, uint8_t* mask_out, int batch, int block_len,
+                              int vocab, float* conf_out, int32_t* pred_out,
+                              const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }  /* extern "C" */
 #endif

@@ -136,6 +136,44 @@ def test_unmask_halves_validate():
                                 None) == B.TT_EINVAL
 
 
+SELECT_BAD = [
+    dict(mode="top_k", k=-1),
+    dict(mode="leftmost", k=-3),
+    dict(mode="threshold", gamma=float("nan"), steps_left=2),
+    dict(mode="threshold", gamma=float("inf"), steps_left=2),
+    dict(mode="threshold", gamma=0.8, steps_left=0),
+    dict(mode="schedule", step=0, n_steps=4),
+    dict(mode="schedule", step=5, n_steps=4),
+    dict(mode="schedule", step=1, n_steps=0),
+]
+
+
+@pytest.mark.parametrize("kw", SELECT_BAD, ids=[str(k) for k in SELECT_BAD])
+def test_select_rules_validate(kw):
+    lib = tt.lib()
+    sel = tt.select_rule(**kw)
+    assert lib.tt_unmask_step_ex(FAKE, FAKE, ctypes.byref(sel), FAKE, FAKE, 1, 16, 1000, None,
+                                 None, FAKE, 1 << 20, None) == B.TT_EINVAL
+    assert lib.tt_unmask_commit_ex(FAKE, ctypes.byref(sel), FAKE, FAKE, 1, 16, 1000, None, None,
+                                   FAKE, 1 << 20, None) == B.TT_EINVAL
+
+
+def test_select_rule_struct_and_unknown_mode():
+    lib = tt.lib()
+    bad = B.Select(9, 1, 0.0, 1, 1, 1)
+    assert lib.tt_unmask_step_ex(FAKE, FAKE, ctypes.byref(bad), FAKE, FAKE, 1, 16, 1000, None,
+                                 None, FAKE, 1 << 20, None) == B.TT_EINVAL
+    assert lib.tt_unmask_step_ex(FAKE, FAKE, None, FAKE, FAKE, 1, 16, 1000, None, None, FAKE,
+                                 1 << 20, None) == B.TT_EINVAL
+    # Empty batch with a valid rule: nothing to do.
+    ok = tt.select_rule("threshold", gamma=0.8, steps_left=3)
+    assert lib.tt_unmask_step_ex(None, FAKE, ctypes.byref(ok), None, None, 0, 16, 1000, None, None,
+                                 None, 0, None) == B.TT_OK
+    assert ctypes.sizeof(B.Select) == 24
+    with pytest.raises(ValueError):
+        tt.select_rule("greedy")
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "nope.so"))
