@@ -15,6 +15,9 @@ equations and algorithms are garbled by text extraction, and the readings
 taken are stated next to each function.
 
 * ``block_attn``   -- TwoTower paper §2.1 "Bidirectional Attention", Eq. (1).
+* ``block_attn_varlen`` -- Eq. (1) with a prefix length per batch entry.
+* ``block_attn_multiblock`` -- the training-style pass over all noisy blocks
+  of a sequence (§2.3 "Training", Implementation paragraph).
 * ``vocab_stats``  -- TwoTower paper §2.2 "Sampling" (confidence of the
   prediction at each masked position) and Algorithm 2 (the denoiser's
   distribution p_theta).
@@ -30,10 +33,10 @@ Pins: every function here is checked by the ``-m "not gpu"`` tests against
 brute force in 50-digit arithmetic, closed forms, invariants and library
 routines (tests/test_oracle_*.py).  No function is "parity unpinned".
 """
-from .block_attn import block_attn, decode_bf16
+from .block_attn import block_attn, block_attn_multiblock, block_attn_varlen, decode_bf16
 from .unmask import (LEFTMOST, SCHEDULE, THRESHOLD, TOP_K, commit_count, select_step, topk_select,
                      unmask_step, unmask_step_select, vocab_stats)
 
-__all__ = ["block_attn", "decode_bf16", "vocab_stats", "unmask_step", "topk_select",
+__all__ = ["block_attn", "block_attn_varlen", "block_attn_multiblock", "decode_bf16", "vocab_stats", "unmask_step", "topk_select",
            "unmask_step_select", "select_step", "commit_count", "TOP_K", "THRESHOLD", "SCHEDULE",
            "LEFTMOST"]

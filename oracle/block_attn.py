@@ -99,3 +99,79 @@ def block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, *,
     if return_weights:
         return out, lse, weights
     return out, lse
+
+
+def block_attn_varlen(q, k_ctx, v_ctx, prefix_lens, k_blk, v_blk, scale):
+    """Eq. (1) where every batch entry b has its own prefix length P_b (a batch
+    of sequences generated to different lengths).  Entry b sees cache rows
+    0..P_b-1 and all of its block rows; everything else is as in block_attn,
+    which is applied to each entry on its own.
+
+    prefix_lens: [B] integers, 0 <= P_b <= Pcap.  Returns (out, lse)."""
+    q = np.asarray(q, dtype=np.float64)
+    B = q.shape[0]
+    lens = [int(p) for p in np.asarray(prefix_lens).reshape(-1)]
+    if len(lens) != B:
+        raise ValueError("one prefix length per batch entry")
+    outs, lses = [], []
+    for b in range(B):
+        o, s = block_attn(q[b:b + 1], k_ctx[b:b + 1], v_ctx[b:b + 1], lens[b], k_blk[b:b + 1],
+                          v_blk[b:b + 1], scale)
+        outs.append(o)
+        lses.append(s)
+    return np.concatenate(outs, axis=0), np.concatenate(lses, axis=0)
+
+
+def block_attn_multiblock(q, k_ctx, v_ctx, k_noisy, v_noisy, block_size, scale):
+    """The denoiser's training-style pass over all noisy blocks of a sequence
+    at once (TwoTower paper §2.3 "Training", Implementation paragraph; the
+    visibility of §2.1 Eq. (1) applied to every block): with blocks of S =
+    block_size rows, query row t of block j = t // S sees the clean context
+    tower's rows 0..j*S-1 (the clean blocks before j) and the noisy rows
+    j*S..(j+1)*S-1 of its own block (bidirectionally); nothing else.
+
+      q        [B, Hq, N*S, D]   noisy queries, N blocks
+      k_ctx    [B, Hkv, Tc, D]   context tower K of the clean sequence, Tc >= (N-1)*S
+      v_ctx    same
+      k_noisy  [B, Hkv, N*S, D]  denoiser K of the noisy blocks
+      v_noisy  same
+
+    Method: one key axis [context rows 0..Tc-1 ; noisy rows 0..N*S-1], an
+    explicit per-row visibility mask, the full score matrix, a row softmax
+    and the weighted sum of values, per (batch, query head).  Returns
+    (out [B,Hq,N*S,D], lse [B,Hq,N*S])."""
+    q = np.asarray(q, dtype=np.float64)
+    k_ctx = np.asarray(k_ctx, dtype=np.float64)
+    v_ctx = np.asarray(v_ctx, dtype=np.float64)
+    k_noisy = np.asarray(k_noisy, dtype=np.float64)
+    v_noisy = np.asarray(v_noisy, dtype=np.float64)
+    B, Hq, T, D = q.shape
+    Hkv, Tc = k_ctx.shape[1], k_ctx.shape[2]
+    S = int(block_size)
+    if S < 1 or T % S != 0:
+        raise ValueError("the query length must be a whole number of blocks")
+    N = T // S
+    if Hq % Hkv != 0 or Tc < (N - 1) * S:
+        raise ValueError("head counts or context length do not fit")
+    if k_noisy.shape != (B, Hkv, T, D) or v_noisy.shape != (B, Hkv, T, D):
+        raise ValueError("noisy K/V shape mismatch")
+    G = Hq // Hkv
+    blk = np.arange(T) // S                                      # block of each query / noisy row
+    visible = np.zeros((T, Tc + T), dtype=bool)
+    visible[:, :Tc] = np.arange(Tc)[None, :] < (blk * S)[:, None]   # clean rows before the block
+    visible[:, Tc:] = blk[None, :] == blk[:, None]                  # own noisy block
+    out = np.empty((B, Hq, T, D), dtype=np.float64)
+    lse = np.empty((B, Hq, T), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            K = np.concatenate([k_ctx[b, g], k_noisy[b, g]], axis=0)
+            V = np.concatenate([v_ctx[b, g], v_noisy[b, g]], axis=0)
+            Sc = np.where(visible, scale * (q[b, h] @ K.T), -np.inf)
+            row_max = Sc.max(axis=1, keepdims=True)
+            E = np.exp(Sc - row_max)
+            den = E.sum(axis=1, keepdims=True)
+            W = E / den
+            out[b, h] = np.where(visible, W, 0.0) @ np.where(visible.any(axis=0)[:, None], V, 0.0)
+            lse[b, h] = row_max[:, 0] + np.log(den[:, 0])
+    return out, lse
