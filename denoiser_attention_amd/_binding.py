@@ -64,6 +64,12 @@ _SIGNATURES = {
                            _vp, _sz, _vp]),
     "tt_block_attn_ex": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i, _i, _i,
                               _i, _vp, _sz, _vp, ctypes.POINTER(AttnOpts)]),
+    "tt_block_attn_varlen": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _f, _vp, _i,
+                                  _i, _i, _i, _vp, _sz, _vp, ctypes.POINTER(AttnOpts)]),
+    "tt_block_attn_multiblock_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i,
+                                                       ctypes.POINTER(AttnOpts)]),
+    "tt_block_attn_multiblock": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i,
+                                      _i, _i, _i, _vp, _sz, _vp, ctypes.POINTER(AttnOpts)]),
     "tt_unmask_workspace_bytes": (_sz, [_i, _i, _i]),
     "tt_unmask_step": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "tt_unmask_reduce": (_i, [_vp, _vp, _i, _i, _i, _vp, _sz, _vp]),
@@ -190,6 +196,110 @@ def block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, *, out=None, ou
         float(scale), _ptr(out), B, Pcap, _dtype_code(q.dtype), _dtype_code(out.dtype),
         _ptr(workspace), ws_bytes, _stream(device, stream), ctypes.byref(opts))
     _check(st, "tt_block_attn")
+    return out
+
+
+def _ctx_checks(k_ctx, v_ctx, q, B, Hkv, D, device, need_rows):
+    if k_ctx is None or v_ctx is None:
+        _require(k_ctx is None and v_ctx is None and need_rows == 0,
+                 "k_ctx/v_ctx may be omitted only when no cache row is visible")
+        return 0
+    for name, t in (("k_ctx", k_ctx), ("v_ctx", v_ctx)):
+        _cuda_contig(name, t, device)
+        _require(t.dtype == q.dtype, f"{name} dtype differs from q")
+    _require(k_ctx.dim() == 4 and k_ctx.shape[0] == B and k_ctx.shape[1] == Hkv
+             and k_ctx.shape[3] == D, "k_ctx must be [B, Hkv, cap, D]")
+    _require(v_ctx.shape == k_ctx.shape, "v_ctx must match k_ctx")
+    return k_ctx.shape[2]
+
+
+def block_attn_varlen(q, k_ctx, v_ctx, prefix_lens, max_prefix_len, k_blk, v_blk, scale, *,
+                      out=None, out_dtype=None, path: str = "auto", kv_splits: int = 0,
+                      kv_groups: int = 0, workspace=None, stream=None):
+    """Eq. (1) with a prefix length per batch entry (tt_block_attn_varlen).
+    ``prefix_lens`` is an int32 tensor [B] on the same GPU, every value in
+    [0, max_prefix_len]."""
+    _require(q.dim() == 4, "q must be [B, Hq, L, D]")
+    device = q.device
+    B, Hq, L, D = q.shape
+    for name, t in (("q", q), ("k_blk", k_blk), ("v_blk", v_blk)):
+        _cuda_contig(name, t, device)
+        _require(t.dtype == q.dtype, f"{name} dtype differs from q")
+    _require(k_blk.dim() == 4 and k_blk.shape[0] == B and k_blk.shape[2] == L
+             and k_blk.shape[3] == D and v_blk.shape == k_blk.shape, "k_blk/v_blk: [B, Hkv, L, D]")
+    Hkv = k_blk.shape[1]
+    _cuda_contig("prefix_lens", prefix_lens, device)
+    _require(prefix_lens.dtype == torch.int32 and tuple(prefix_lens.shape) == (B,),
+             "prefix_lens: int32 [B]")
+    Pcap = _ctx_checks(k_ctx, v_ctx, q, B, Hkv, D, device, max_prefix_len)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, Hq, L, D), dtype=out_dtype, device=device)
+    _cuda_contig("out", out, device)
+    _require(tuple(out.shape) == (B, Hq, L, D), "out must be [B, Hq, L, D]")
+    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups)
+    need = attn_workspace_bytes(B, max_prefix_len, L, Hq, Hkv, D, q.dtype, path, kv_splits,
+                                kv_groups)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().tt_block_attn_varlen(
+        _ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(prefix_lens), int(max_prefix_len), _ptr(k_blk),
+        _ptr(v_blk), L, Hq, Hkv, D, float(scale), _ptr(out), B, Pcap, _dtype_code(q.dtype),
+        _dtype_code(out.dtype), _ptr(workspace), ws_bytes, _stream(device, stream),
+        ctypes.byref(opts))
+    _check(st, "tt_block_attn_varlen")
+    return out
+
+
+def attn_multiblock_workspace_bytes(batch, block_size, n_blocks, n_q_heads, n_kv_heads, head_dim,
+                                    dtype: torch.dtype, path: str = "auto", kv_splits: int = 0,
+                                    kv_groups: int = 0) -> int:
+    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups)
+    n = lib().tt_block_attn_multiblock_workspace_bytes(batch, block_size, n_blocks, n_q_heads,
+                                                       n_kv_heads, head_dim, _dtype_code(dtype),
+                                                       ctypes.byref(opts))
+    if n == SIZE_MAX:
+        raise ValueError("invalid attention shape")
+    return n
+
+
+def block_attn_multiblock(q, k_ctx, v_ctx, k_noisy, v_noisy, block_size, scale, *, out=None,
+                          out_dtype=None, path: str = "auto", kv_splits: int = 0,
+                          kv_groups: int = 0, workspace=None, stream=None):
+    """Training-style pass over all noisy blocks (tt_block_attn_multiblock).
+    q [B,Hq,N*S,D]; k_ctx/v_ctx [B,Hkv,cap,D] with cap >= (N-1)*S;
+    k_noisy/v_noisy [B,Hkv,N*S,D]."""
+    _require(q.dim() == 4, "q must be [B, Hq, N*S, D]")
+    device = q.device
+    B, Hq, T, D = q.shape
+    S = int(block_size)
+    _require(S >= 1 and T % S == 0, "the query length must be a whole number of blocks")
+    N = T // S
+    for name, t in (("q", q), ("k_noisy", k_noisy), ("v_noisy", v_noisy)):
+        _cuda_contig(name, t, device)
+        _require(t.dtype == q.dtype, f"{name} dtype differs from q")
+    _require(k_noisy.dim() == 4 and k_noisy.shape[0] == B and k_noisy.shape[2] == T
+             and k_noisy.shape[3] == D and v_noisy.shape == k_noisy.shape,
+             "k_noisy/v_noisy: [B, Hkv, N*S, D]")
+    Hkv = k_noisy.shape[1]
+    cap = _ctx_checks(k_ctx, v_ctx, q, B, Hkv, D, device, (N - 1) * S)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, Hq, T, D), dtype=out_dtype, device=device)
+    _cuda_contig("out", out, device)
+    _require(tuple(out.shape) == (B, Hq, T, D), "out must be [B, Hq, N*S, D]")
+    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups)
+    need = attn_multiblock_workspace_bytes(B, S, N, Hq, Hkv, D, q.dtype, path, kv_splits,
+                                           kv_groups)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().tt_block_attn_multiblock(
+        _ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(k_noisy), _ptr(v_noisy), S, N, Hq, Hkv, D,
+        float(scale), _ptr(out), B, cap, _dtype_code(q.dtype), _dtype_code(out.dtype),
+        _ptr(workspace), ws_bytes, _stream(device, stream), ctypes.byref(opts))
+    _check(st, "tt_block_attn_multiblock")
     return out
 
 

@@ -162,16 +162,25 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   const int lr = lane & 31, hh = lane >> 5;     // MFMA row/column lane, lane half
   const int grp = lane >> 4, gi = lane & 15;    // 16-lane group, index in group
 
-  int logical = xcd_remap(blockIdx.x, n_blocks);
+  // Items of the multi-block pass differ in length: they are taken longest
+  // first and spread over all XCDs instead of grouped per XCD.
+  int logical = p.prefix_mode == 2 ? (int)blockIdx.x : xcd_remap(blockIdx.x, n_blocks);
   const int mt = logical % m_tiles;
   logical /= m_tiles;
   const int split = logical % p.splits;
-  const int pair = logical / p.splits;       // b * Hkv + kv head
-  const int b = pair / p.Hkv, kvh = pair - b * p.Hkv;
+  const int pair = logical / p.splits;       // item * Hkv + kv head
+  int w = pair / p.Hkv;
+  const int kvh = pair - w * p.Hkv;
+  if (p.prefix_mode == 2) {
+    const int bb = w / p.NB;
+    w = bb * p.NB + (p.NB - 1 - (w - bb * p.NB));
+  }
+  const AttnItem it = attn_item(p, w, kvh);
 
-  const int n_keys = p.n_keys, P = p.P;
+  const int n_keys = it.n_keys, P = it.P;
   const int n_tiles = (n_keys + BN - 1) / BN;
   const int wg_begin = split * p.tiles_per_split;
+  if (wg_begin >= n_tiles) return;   // this item has fewer splits (whole workgroup)
   const int wg_end = min(n_tiles, wg_begin + p.tiles_per_split);
   const int wg_n = wg_end - wg_begin;
   const int n_lead = KG == 1 ? 0 : wg_n / 2;        // tiles of group 0 when KG == 2
@@ -180,13 +189,13 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   const int cnt = t_end - t_begin;                  // this group's tiles (may be 0)
   const int nit = wg_n - n_lead;                    // iterations, equal for every group
 
-  const char* kc = static_cast<const char*>(p.k_ctx) + (size_t)pair * p.Pcap * L::ROWB;
-  const char* vc = static_cast<const char*>(p.v_ctx) + (size_t)pair * p.Pcap * L::ROWB;
-  const char* kb = static_cast<const char*>(p.k_blk) + (size_t)pair * p.L * L::ROWB;
-  const char* vb = static_cast<const char*>(p.v_blk) + (size_t)pair * p.L * L::ROWB;
+  const char* kc = static_cast<const char*>(p.k_ctx) + it.ctx_row0 * L::ROWB;
+  const char* vc = static_cast<const char*>(p.v_ctx) + it.ctx_row0 * L::ROWB;
+  const char* kb = static_cast<const char*>(p.k_blk) + it.blk_row0 * L::ROWB;
+  const char* vb = static_cast<const char*>(p.v_blk) + it.blk_row0 * L::ROWB;
 
-  // First row of this pair in the flattened [B*Hq*L] row space.
-  const size_t row_base = ((size_t)b * p.Hq + (size_t)kvh * p.G) * p.L;
+  // Packed row index of this (item, kv head)'s row 0 (split partials).
+  const size_t prow_base = ((size_t)w * p.Hkv + kvh) * p.M;
   const int wave_row0 = mt * BM + wave * 32;
   const int r_local = wave_row0 + lr;
   const bool row_ok = r_local < p.M;
@@ -195,8 +204,8 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // Q fragments: lane holds row r_local, columns 16s + 8hh .. +7 for every s.
   bf16x8 qf[L::DS];
   {
-    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.q) +
-                                                      (row_base + (row_ok ? r_local : 0)) * D);
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        static_cast<const uint16_t*>(p.q) + (it.q_head0 + attn_row_off(p, row_ok ? r_local : 0)) * D);
 #pragma unroll
     for (int s = 0; s < L::DS; ++s) {
       const u32x4 v = row_ok ? src[2 * s + hh] : u32x4{0, 0, 0, 0};
@@ -467,7 +476,6 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     }
   asm volatile("" ::: "memory");
   const int rows_here = min(32, p.M - wave_row0);   // valid rows of this wave
-  const size_t grow0 = row_base + wave_row0;
   if (OUT_BF16) {
     // 8 values (16 bytes) per lane, D/8 lanes per row.
     constexpr int LPR = D / 8, RPI = 64 / LPR;
@@ -481,24 +489,30 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
       pk.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a.z) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a.w) << 16);
       pk.z = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.x) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.y) << 16);
       pk.w = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.z) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.w) << 16);
-      if (row < rows_here)
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + (grow0 + row) * D + 8 * c8) = pk;
+      if (row < rows_here) {
+        const size_t orow = it.q_head0 + attn_row_off(p, wave_row0 + row);
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + orow * D + 8 * c8) = pk;
+      }
     }
   } else {
     // 4 values (16 bytes) per lane, D/4 lanes per row: the final fp32 output,
     // or this split's partial.
     constexpr int LPR = D / 4, RPI = 64 / LPR;
-    const size_t rows_total = (size_t)p.B * p.Hq * p.L;
-    float* dst = p.splits == 1 ? static_cast<float*>(p.out) + grow0 * D
-                               : p.part_o + ((size_t)split * rows_total + grow0) * D;
+    const size_t rows_total = (size_t)p.B * p.NB * p.Hq * p.L;
+    float* part = p.part_o + ((size_t)split * rows_total + prow_base + wave_row0) * D;
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
       const int row = i * RPI + lane / LPR, c4 = lane % LPR;
       const f32x4 v = *reinterpret_cast<const f32x4*>(stg + row * D + ((c4 ^ (row & 7)) << 2));
-      if (row < rows_here) *reinterpret_cast<f32x4*>(dst + (size_t)row * D + 4 * c4) = v;
+      if (row < rows_here) {
+        float* dst = p.splits == 1
+                         ? static_cast<float*>(p.out) + (it.q_head0 + attn_row_off(p, wave_row0 + row)) * D
+                         : part + (size_t)row * D;
+        *reinterpret_cast<f32x4*>(dst + 4 * c4) = v;
+      }
     }
     if (p.splits > 1 && hh == 0 && row_ok)
-      p.part_lse[(size_t)split * rows_total + row_base + r_local] = m_run + __log2f(l_tot);
+      p.part_lse[(size_t)split * rows_total + prow_base + r_local] = m_run + __log2f(l_tot);
   }
 }
 
@@ -507,7 +521,7 @@ constexpr int kStages = 4;
 template <int D, bool OUT_BF16, bool POS>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   const int m_tiles = (p.M + BM - 1) / BM;
-  const long long n = (long long)m_tiles * p.splits * p.B * p.Hkv;
+  const long long n = (long long)m_tiles * p.splits * p.B * p.NB * p.Hkv;
   if (n <= 0 || n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (p.kgroups == 2)
     hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 2, OUT_BF16, POS>), dim3((unsigned)n),

@@ -105,18 +105,20 @@ __global__ __launch_bounds__(64) void attn_shuffle_kernel(AttnParams p, int row_
   const int rt = logical % row_tiles;
   logical /= row_tiles;
   const int split = logical % p.splits;
-  const int pair = logical / p.splits;
-  const int b = pair / p.Hkv, kvh = pair % p.Hkv;
+  const int pair = logical / p.splits;       // item * Hkv + kv head
+  const int w = pair / p.Hkv, kvh = pair % p.Hkv;
+  const AttnItem it = attn_item(p, w, kvh);
 
-  const int n_keys = p.n_keys, P = p.P;
+  const int n_keys = it.n_keys, P = it.P;
   const int k_begin = split * p.tiles_per_split * BNS;
+  if (k_begin >= n_keys) return;   // this item has fewer splits (whole workgroup)
   const int k_end = min(n_keys, k_begin + p.tiles_per_split * BNS);
 
-  const T* kc = static_cast<const T*>(p.k_ctx) + (size_t)pair * p.Pcap * D;
-  const T* vc = static_cast<const T*>(p.v_ctx) + (size_t)pair * p.Pcap * D;
-  const T* kb = static_cast<const T*>(p.k_blk) + (size_t)pair * p.L * D;
-  const T* vb = static_cast<const T*>(p.v_blk) + (size_t)pair * p.L * D;
-  const size_t row_base = ((size_t)b * p.Hq + (size_t)kvh * p.G) * p.L;
+  const T* kc = static_cast<const T*>(p.k_ctx) + it.ctx_row0 * D;
+  const T* vc = static_cast<const T*>(p.v_ctx) + it.ctx_row0 * D;
+  const T* kb = static_cast<const T*>(p.k_blk) + it.blk_row0 * D;
+  const T* vb = static_cast<const T*>(p.v_blk) + it.blk_row0 * D;
+  const size_t prow_base = ((size_t)w * p.Hkv + kvh) * p.M;   // packed row of row 0
   const int r0 = rt * R;
 
   // Query slices, pre-multiplied by scale*log2(e) (fp32 arithmetic).
@@ -124,7 +126,8 @@ __global__ __launch_bounds__(64) void attn_shuffle_kernel(AttnParams p, int row_
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (r0 + r < p.M) {
-      load_slice<T, E>(static_cast<const T*>(p.q) + (row_base + r0 + r) * D + li * E, q[r]);
+      load_slice<T, E>(static_cast<const T*>(p.q) + (it.q_head0 + attn_row_off(p, r0 + r)) * D +
+                           li * E, q[r]);
 #pragma unroll
       for (int e = 0; e < E; ++e) q[r][e] *= p.scale_log2;
     } else {
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(64) void attn_shuffle_kernel(AttnParams p, int row_
     for (int e = 0; e < E; ++e) s_o[grp][r][li * E + e] = o[r][e];
   __syncthreads();
 
-  const size_t rows_total = (size_t)p.B * p.Hq * p.L;
+  const size_t rows_total = (size_t)p.B * p.NB * p.Hq * p.L;
   for (int idx = lane; idx < R * D; idx += 64) {
     const int r = idx / D, d = idx % D;
     if (r0 + r >= p.M) continue;
@@ -193,9 +196,9 @@ __global__ __launch_bounds__(64) void attn_shuffle_kernel(AttnParams p, int row_
       lt = fmaf(s_l[g][r], w, lt);
       ot = fmaf(s_o[g][r][d], w, ot);
     }
-    const size_t grow = row_base + r0 + r;
+    const size_t grow = prow_base + r0 + r;
     if (p.splits == 1) {
-      store_out<TO>(p.out, grow * D + d, ot / lt);
+      store_out<TO>(p.out, (it.q_head0 + attn_row_off(p, r0 + r)) * D + d, ot / lt);
     } else {
       p.part_o[((size_t)split * rows_total + grow) * D + d] = ot / lt;
       if (d == 0) p.part_lse[(size_t)split * rows_total + grow] = mx + __log2f(lt);
@@ -211,20 +214,24 @@ constexpr int kMergeBatch = 8;
 
 template <typename TO>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
-  const size_t rows = (size_t)p.B * p.Hq * p.L;
+  const size_t rows = (size_t)p.B * p.NB * p.Hq * p.L;
   const int groups = p.D / 4;
   const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= rows * groups) return;
-  const size_t row = gid / groups;
+  const size_t row = gid / groups;          // packed row ((item * Hkv + kvh) * M + r)
   const int g = (int)(gid % groups);
+  const int pair = (int)(row / p.M), r = (int)(row - (size_t)pair * p.M);
+  const int w = pair / p.Hkv, kvh = pair - w * p.Hkv;
+  const AttnItem it = attn_item(p, w, kvh);
+  const int n_splits = attn_item_splits(p, it.n_keys);   // splits that hold keys of this item
   float m = -INFINITY, wsum = 0.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < p.splits; s0 += kMergeBatch) {
+  for (int s0 = 0; s0 < n_splits; s0 += kMergeBatch) {
     float lse[kMergeBatch];
     f32x4 o[kMergeBatch];
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
-      if (s0 + i < p.splits) {
+      if (s0 + i < n_splits) {
         const size_t r = (size_t)(s0 + i) * rows + row;
         lse[i] = p.part_lse[r];
         o[i] = *reinterpret_cast<const f32x4*>(p.part_o + r * p.D + 4 * g);
@@ -232,7 +239,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
     }
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
-      if (s0 + i < p.splits) {
+      if (s0 + i < n_splits) {
         const float m_new = fmaxf(m, lse[i]);
         const float a = __builtin_amdgcn_exp2f(m - m_new);       // 0 on the first split
         const float w = __builtin_amdgcn_exp2f(lse[i] - m_new);
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
     }
   }
   const float inv = 1.0f / wsum;
-  const size_t base = row * p.D + 4 * g;
+  const size_t base = (it.q_head0 + attn_row_off(p, r)) * p.D + 4 * g;
 #pragma unroll
   for (int i = 0; i < 4; ++i) store_out<TO>(p.out, base + i, acc[i] * inv);
 }
@@ -251,7 +258,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
 template <int D, typename T, typename TO>
 hipError_t launch_shuf(const AttnParams& p, hipStream_t stream) {
   const int row_tiles = (p.M + R - 1) / R;
-  const long long n = (long long)row_tiles * p.splits * p.B * p.Hkv;
+  const long long n = (long long)row_tiles * p.splits * p.B * p.NB * p.Hkv;
   if (n <= 0 || n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((attn_shuffle_kernel<D, T, TO>), dim3((unsigned)n), dim3(64), 0, stream, p,
                      row_tiles);
@@ -282,7 +289,7 @@ hipError_t launch_attn_shuffle(const AttnParams& p, int in_bf16, hipStream_t str
 }
 
 hipError_t launch_attn_merge(const AttnParams& p, hipStream_t stream) {
-  const size_t n = (size_t)p.B * p.Hq * p.L * (p.D / 4);
+  const size_t n = (size_t)p.B * p.NB * p.Hq * p.L * (p.D / 4);
   const size_t blocks = (n + 255) / 256;
   if (blocks == 0 || blocks > 0x7fffffffULL) return hipErrorInvalidConfiguration;
   if (p.out_bf16) {

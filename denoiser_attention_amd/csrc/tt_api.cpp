@@ -50,9 +50,12 @@ struct AttnPlan {
 bool mfma_head_dim(int d) { return d == 64 || d == 128; }
 bool shuffle_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
 
-tt_status plan_attn(int B, int P, int L, int Hq, int Hkv, int D, tt_dtype dtype,
+// B counts work items (batch entries times blocks per entry); P is the
+// longest item's prefix.
+tt_status plan_attn(long long B, int P, int L, int Hq, int Hkv, int D, tt_dtype dtype,
                     const tt_attn_opts* opts, AttnPlan* plan) {
   if (B < 0 || P < 0 || L < 0 || Hq < 1 || Hkv < 1 || D < 1) return TT_EINVAL;
+  if (B > INT_MAX) return TT_EUNSUPPORTED;
   if (Hq % Hkv != 0) return TT_EINVAL;
   if (dtype != TT_FP32 && dtype != TT_BF16) return TT_EINVAL;
   const int req = opts ? opts->path : TT_ATTN_AUTO;
@@ -180,6 +183,96 @@ TT_EXPORT size_t tt_block_attn_workspace_bytes(int batch, int prefix_len, int bl
   return plan.ws_bytes;
 }
 
+namespace {
+
+// One attention call in any of its three forms.
+struct AttnCall {
+  const void *q, *k_ctx, *v_ctx, *k_blk, *v_blk;
+  void* out;
+  const int32_t* prefix_lens;   // mode 1
+  int prefix_mode;              // 0 uniform, 1 per batch entry, 2 multi-block
+  int P;                        // mode 0: the prefix; mode 1: the bound; mode 2: unused
+  int L, NB, Hq, Hkv, D, batch, Pcap;
+  float scale;
+  tt_dtype dtype, out_dtype;
+  void* workspace;
+  size_t workspace_bytes;
+  hipStream_t stream;
+  const tt_attn_opts* opts;
+};
+
+// Longest prefix of any item of the call.
+int call_max_prefix(const AttnCall& c) {
+  return c.prefix_mode == 2 ? (c.NB > 0 ? (c.NB - 1) * c.L : 0) : c.P;
+}
+
+tt_status attn_run(const AttnCall& c) {
+  if (c.NB < 0 || c.L < 0) return TT_EINVAL;
+  if (c.prefix_mode == 2 && (long long)c.NB * c.L > INT_MAX / 2) return TT_EUNSUPPORTED;
+  const int Pmax = call_max_prefix(c);
+  AttnPlan plan;
+  tt_status st = plan_attn((long long)c.batch * c.NB, Pmax, c.L, c.Hq, c.Hkv, c.D, c.dtype,
+                           c.opts, &plan);
+  if (st != TT_OK) return st;
+  if (c.Pcap < Pmax) return TT_EINVAL;
+  if (!std::isfinite(c.scale)) return TT_EINVAL;
+  if (c.out_dtype != TT_FP32 && c.out_dtype != TT_BF16) return TT_EINVAL;
+  if (c.dtype == TT_FP32 && c.out_dtype != TT_FP32) return TT_EINVAL;
+  if (plan.empty) return TT_OK;
+  if (!c.q || !c.k_blk || !c.v_blk || !c.out) return TT_EINVAL;
+  if (c.Pcap > 0 && (!c.k_ctx || !c.v_ctx)) return TT_EINVAL;
+  if (c.prefix_mode == 1 && !c.prefix_lens) return TT_EINVAL;
+  if (plan.ws_bytes > 0 && (!c.workspace || c.workspace_bytes < plan.ws_bytes)) return TT_EINVAL;
+  st = device_present();
+  if (st != TT_OK) return st;
+
+  AttnParams p{};
+  p.q = c.q;
+  p.k_ctx = c.k_ctx;
+  p.v_ctx = c.v_ctx;
+  p.k_blk = c.k_blk;
+  p.v_blk = c.v_blk;
+  p.out = c.out;
+  p.prefix_lens = c.prefix_lens;
+  p.B = c.batch;
+  p.Hq = c.Hq;
+  p.Hkv = c.Hkv;
+  p.G = c.Hq / c.Hkv;
+  p.L = c.L;
+  p.P = Pmax;
+  p.Pcap = c.Pcap;
+  p.D = c.D;
+  p.NB = c.NB;
+  p.T = c.NB * c.L;
+  p.prefix_mode = c.prefix_mode;
+  p.L_magic = c.L == 1 ? 0xffffffffu : (uint32_t)((1ull << 32) / (unsigned)c.L);
+  p.M = p.G * c.L;
+  p.n_keys = Pmax + c.L;
+  p.tile_keys = plan.path == TT_ATTN_MFMA ? tt::kAttnMfmaBN : tt::kAttnShufBN;
+  p.splits = plan.splits;
+  p.tiles_per_split = plan.tiles_per_split;
+  p.kgroups = plan.kgroups;
+  p.out_bf16 = c.out_dtype == TT_BF16 ? 1 : 0;
+  p.scale_log2 = c.scale * kLog2e;
+  if (plan.splits > 1) {
+    p.part_o = static_cast<float*>(c.workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(c.workspace) + plan.lse_offset);
+  }
+
+  (void)hipGetLastError();  // clear any stale error so it is not reported as ours
+  hipError_t e = plan.path == TT_ATTN_MFMA
+                     ? tt::launch_attn_mfma(p, c.stream)
+                     : tt::launch_attn_shuffle(p, c.dtype == TT_BF16, c.stream);
+  if (e != hipSuccess) return TT_EHIP;
+  if (plan.splits > 1) {
+    e = tt::launch_attn_merge(p, c.stream);
+    if (e != hipSuccess) return TT_EHIP;
+  }
+  return TT_OK;
+}
+
+}  // namespace
+
 TT_EXPORT tt_status tt_block_attn_ex(const void* q, const void* k_ctx, const void* v_ctx,
                                      int prefix_len, const void* k_blk, const void* v_blk,
                                      int block_len, int n_q_heads, int n_kv_heads, int head_dim,
@@ -187,57 +280,11 @@ TT_EXPORT tt_status tt_block_attn_ex(const void* q, const void* k_ctx, const voi
                                      tt_dtype dtype, tt_dtype out_dtype, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream,
                                      const tt_attn_opts* opts) {
-  AttnPlan plan;
-  tt_status st = plan_attn(batch, prefix_len, block_len, n_q_heads, n_kv_heads, head_dim, dtype,
-                           opts, &plan);
-  if (st != TT_OK) return st;
-  if (prefix_cap < prefix_len) return TT_EINVAL;
-  if (!std::isfinite(scale)) return TT_EINVAL;
-  if (out_dtype != TT_FP32 && out_dtype != TT_BF16) return TT_EINVAL;
-  if (dtype == TT_FP32 && out_dtype != TT_FP32) return TT_EINVAL;
-  if (plan.empty) return TT_OK;
-  if (!q || !k_blk || !v_blk || !out) return TT_EINVAL;
-  if (prefix_cap > 0 && (!k_ctx || !v_ctx)) return TT_EINVAL;
-  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return TT_EINVAL;
-  st = device_present();
-  if (st != TT_OK) return st;
-
-  AttnParams p{};
-  p.q = q;
-  p.k_ctx = k_ctx;
-  p.v_ctx = v_ctx;
-  p.k_blk = k_blk;
-  p.v_blk = v_blk;
-  p.out = out;
-  p.B = batch;
-  p.Hq = n_q_heads;
-  p.Hkv = n_kv_heads;
-  p.G = n_q_heads / n_kv_heads;
-  p.L = block_len;
-  p.P = prefix_len;
-  p.Pcap = prefix_cap;
-  p.D = head_dim;
-  p.M = p.G * block_len;
-  p.n_keys = prefix_len + block_len;
-  p.splits = plan.splits;
-  p.tiles_per_split = plan.tiles_per_split;
-  p.kgroups = plan.kgroups;
-  p.out_bf16 = out_dtype == TT_BF16 ? 1 : 0;
-  p.scale_log2 = scale * kLog2e;
-  if (plan.splits > 1) {
-    p.part_o = static_cast<float*>(workspace);
-    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.lse_offset);
-  }
-
-  (void)hipGetLastError();  // clear any stale error so it is not reported as ours
-  hipError_t e = plan.path == TT_ATTN_MFMA ? tt::launch_attn_mfma(p, stream)
-                                           : tt::launch_attn_shuffle(p, dtype == TT_BF16, stream);
-  if (e != hipSuccess) return TT_EHIP;
-  if (plan.splits > 1) {
-    e = tt::launch_attn_merge(p, stream);
-    if (e != hipSuccess) return TT_EHIP;
-  }
-  return TT_OK;
+  if (prefix_len < 0) return TT_EINVAL;
+  AttnCall c{q, k_ctx, v_ctx, k_blk, v_blk, out, nullptr, 0, prefix_len, block_len, 1,
+             n_q_heads, n_kv_heads, head_dim, batch, prefix_cap, scale, dtype, out_dtype,
+             workspace, workspace_bytes, stream, opts};
+  return attn_run(c);
 }
 
 TT_EXPORT tt_status tt_block_attn(const void* q, const void* k_ctx, const void* v_ctx,
@@ -249,6 +296,50 @@ TT_EXPORT tt_status tt_block_attn(const void* q, const void* k_ctx, const void* 
   return tt_block_attn_ex(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, block_len, n_q_heads,
                           n_kv_heads, head_dim, scale, out, batch, prefix_cap, dtype, out_dtype,
                           workspace, workspace_bytes, stream, nullptr);
+}
+
+TT_EXPORT tt_status tt_block_attn_varlen(const void* q, const void* k_ctx, const void* v_ctx,
+                                         const int32_t* prefix_lens, int max_prefix_len,
+                                         const void* k_blk, const void* v_blk, int block_len,
+                                         int n_q_heads, int n_kv_heads, int head_dim, float scale,
+                                         void* out, int batch, int prefix_cap, tt_dtype dtype,
+                                         tt_dtype out_dtype, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream,
+                                         const tt_attn_opts* opts) {
+  if (max_prefix_len < 0) return TT_EINVAL;
+  AttnCall c{q, k_ctx, v_ctx, k_blk, v_blk, out, prefix_lens, 1, max_prefix_len, block_len, 1,
+             n_q_heads, n_kv_heads, head_dim, batch, prefix_cap, scale, dtype, out_dtype,
+             workspace, workspace_bytes, stream, opts};
+  return attn_run(c);
+}
+
+TT_EXPORT size_t tt_block_attn_multiblock_workspace_bytes(int batch, int block_size,
+                                                          int n_blocks, int n_q_heads,
+                                                          int n_kv_heads, int head_dim,
+                                                          tt_dtype dtype,
+                                                          const tt_attn_opts* opts) {
+  if (batch < 0 || block_size < 0 || n_blocks < 0) return SIZE_MAX;
+  if ((long long)n_blocks * block_size > INT_MAX / 2) return SIZE_MAX;
+  AttnPlan plan;
+  const int Pmax = n_blocks > 0 ? (n_blocks - 1) * block_size : 0;
+  if (plan_attn((long long)batch * n_blocks, Pmax, block_size, n_q_heads, n_kv_heads, head_dim,
+                dtype, opts, &plan) != TT_OK)
+    return SIZE_MAX;
+  return plan.ws_bytes;
+}
+
+TT_EXPORT tt_status tt_block_attn_multiblock(const void* q, const void* k_ctx, const void* v_ctx,
+                                             const void* k_noisy, const void* v_noisy,
+                                             int block_size, int n_blocks, int n_q_heads,
+                                             int n_kv_heads, int head_dim, float scale, void* out,
+                                             int batch, int ctx_cap, tt_dtype dtype,
+                                             tt_dtype out_dtype, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream,
+                                             const tt_attn_opts* opts) {
+  AttnCall c{q, k_ctx, v_ctx, k_noisy, v_noisy, out, nullptr, 2, 0, block_size, n_blocks,
+             n_q_heads, n_kv_heads, head_dim, batch, ctx_cap, scale, dtype, out_dtype,
+             workspace, workspace_bytes, stream, opts};
+  return attn_run(c);
 }
 
 TT_EXPORT size_t tt_unmask_workspace_bytes(int batch, int block_len, int vocab) {

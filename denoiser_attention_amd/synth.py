@@ -151,7 +151,7 @@ def _rng(seed: int, cfg: Config, tensor_id: int, step: int) -> np.random.Generat
 
 # tensor ids for seed derivation
 _T_Q, _T_KCTX, _T_VCTX, _T_KBLK, _T_VBLK, _T_OUTLIER, _T_LOGITS, _T_PLANT, _T_TIE, \
-    _T_GARBAGE = range(10)
+    _T_GARBAGE, _T_LENS = range(11)
 
 
 def attn_inputs(cfg: Config, seed: int = 0, step: int = 0, prefix_len: int | None = None,
@@ -241,3 +241,57 @@ def initial_mask(cfg: Config, batch: int | None = None, block_len: int | None = 
     B = cfg.batch if batch is None else batch
     L = cfg.block_len if block_len is None else block_len
     return np.ones((B, L), dtype=np.uint8)
+
+
+def varlen_inputs(cfg: Config, seed: int = 0, step: int = 0, batch: int | None = None,
+                  max_prefix_len: int | None = None, prefix_cap: int | None = None) -> dict:
+    """attn_inputs for a batch whose entries have different prefix lengths.
+
+    prefix_lens [B] int32: seeded draws in [0, max_prefix_len] with the two
+    extremes (0 and max_prefix_len) always present when B >= 2.  Cache rows
+    past each entry's own length hold +-GARBAGE (they must not be read)."""
+    B = cfg.batch if batch is None else batch
+    Pmax = cfg.prefix_len if max_prefix_len is None else max_prefix_len
+    inp = attn_inputs(cfg, seed=seed, step=step, prefix_len=Pmax, prefix_cap=prefix_cap,
+                      batch=B)
+    r = _rng(seed, cfg, _T_LENS, step)
+    lens = r.integers(0, Pmax + 1, size=B).astype(np.int32)
+    if B >= 2:
+        lens[r.choice(B, size=2, replace=False)] = [0, Pmax]
+    g = np.float32(GARBAGE)
+    gk, gv = (bf16_bits_from_f32(np.array([g, -g], np.float32)) if cfg.dtype == "bf16"
+              else np.array([g, -g], np.float32))
+    for b in range(B):
+        inp["k_ctx"][b, :, lens[b]:, :] = gk
+        inp["v_ctx"][b, :, lens[b]:, :] = gv
+    inp["prefix_lens"] = lens
+    return inp
+
+
+def multiblock_inputs(cfg: Config, n_blocks: int, block_size: int, seed: int = 0, step: int = 0,
+                      batch: int | None = None) -> dict:
+    """Inputs of the training-style pass over all noisy blocks of a sequence:
+    q [B,Hq,N*S,D]; k_ctx/v_ctx [B,Hkv,N*S,D] (the context tower over the
+    clean sequence; the last block's rows are never visible and hold
+    +-GARBAGE); k_noisy/v_noisy [B,Hkv,N*S,D].  Same distributions as
+    attn_inputs."""
+    B = cfg.batch if batch is None else batch
+    T = n_blocks * block_size
+    Hq, Hkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    s = cfg.qkv_std
+
+    def draw(tid, shape):
+        return (_rng(seed, cfg, 100 + tid, step).standard_normal(shape, dtype=np.float32)
+                * np.float32(s))
+
+    out = dict(q=draw(_T_Q, (B, Hq, T, D)), k_ctx=draw(_T_KCTX, (B, Hkv, T, D)),
+               v_ctx=draw(_T_VCTX, (B, Hkv, T, D)), k_noisy=draw(_T_KBLK, (B, Hkv, T, D)),
+               v_noisy=draw(_T_VBLK, (B, Hkv, T, D)))
+    if n_blocks >= 1:
+        out["k_ctx"][:, :, T - block_size:, :] = GARBAGE
+        out["v_ctx"][:, :, T - block_size:, :] = -GARBAGE
+    if cfg.dtype == "bf16":
+        out = {n: bf16_bits_from_f32(a) for n, a in out.items()}
+    out.update(n_blocks=n_blocks, block_size=block_size, batch=B, scale=cfg.softmax_scale,
+               dtype=cfg.dtype)
+    return out

@@ -126,6 +126,48 @@ tt_status tt_block_attn_ex(const void* q, const void* k_ctx, const void* v_ctx, 
                            int prefix_cap, tt_dtype dtype, tt_dtype out_dtype, void* workspace,
                            size_t workspace_bytes, hipStream_t stream, const tt_attn_opts* opts);
 
+/* tt_block_attn_ex where every batch entry b has its own prefix length
+ * prefix_lens[b] (a batch of sequences generated to different lengths): entry
+ * b's queries see cache rows 0..prefix_lens[b]-1 and all of its block rows.
+ *   prefix_lens     DEVICE int32 [batch]; each value in [0, max_prefix_len]
+ *                   (values outside are clamped into that range)
+ *   max_prefix_len  bound on prefix_lens (work is planned for it), <= prefix_cap
+ * Workspace: tt_block_attn_workspace_bytes with prefix_len = max_prefix_len.
+ * All other arguments are those of tt_block_attn_ex. */
+tt_status tt_block_attn_varlen(const void* q, const void* k_ctx, const void* v_ctx,
+                               const int32_t* prefix_lens, int max_prefix_len, const void* k_blk,
+                               const void* v_blk, int block_len, int n_q_heads, int n_kv_heads,
+                               int head_dim, float scale, void* out, int batch, int prefix_cap,
+                               tt_dtype dtype, tt_dtype out_dtype, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream,
+                               const tt_attn_opts* opts);
+
+/* The denoiser's training-style pass over all noisy blocks of a sequence at
+ * once (TwoTower paper §2.3 "Training", Implementation paragraph, with the
+ * visibility of Eq. (1) for every block): the sequence is n_blocks blocks of
+ * S = block_size rows; query row t of block j = t / S attends, under one
+ * softmax, to the context tower's rows 0..j*S-1 (the clean blocks before j)
+ * and to the noisy rows j*S..(j+1)*S-1 of its own block, bidirectionally.
+ *   q        [batch, n_q_heads, n_blocks*S, head_dim]   dtype
+ *   k_ctx    [batch, n_kv_heads, ctx_cap, head_dim]     context tower K of the
+ *            clean sequence; ctx_cap >= (n_blocks-1)*S
+ *   v_ctx    same                                        (both may be NULL if ctx_cap == 0)
+ *   k_noisy  [batch, n_kv_heads, n_blocks*S, head_dim]  denoiser K of the noisy blocks
+ *   v_noisy  same
+ *   out      [batch, n_q_heads, n_blocks*S, head_dim]   out_dtype
+ * Workspace: tt_block_attn_multiblock_workspace_bytes.  Kernel family,
+ * options, dtypes and errors as for tt_block_attn_ex; block_size plays the
+ * role of block_len. */
+size_t tt_block_attn_multiblock_workspace_bytes(int batch, int block_size, int n_blocks,
+                                                int n_q_heads, int n_kv_heads, int head_dim,
+                                                tt_dtype dtype, const tt_attn_opts* opts);
+tt_status tt_block_attn_multiblock(const void* q, const void* k_ctx, const void* v_ctx,
+                                   const void* k_noisy, const void* v_noisy, int block_size,
+                                   int n_blocks, int n_q_heads, int n_kv_heads, int head_dim,
+                                   float scale, void* out, int batch, int ctx_cap, tt_dtype dtype,
+                                   tt_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream, const tt_attn_opts* opts);
+
 /* ------------------------------------------------------------------------ */
 /* Confidence unmask: TwoTower paper §2.2 "Sampling", Algorithm 2.           */
 /* ------------------------------------------------------------------------ */

@@ -136,6 +136,56 @@ def test_unmask_halves_validate():
                                 None) == B.TT_EINVAL
 
 
+def varlen_call(**kw):
+    a = dict(q=FAKE, k_ctx=FAKE, v_ctx=FAKE, lens=FAKE, pmax=64, k_blk=FAKE, v_blk=FAKE, L=16,
+             hq=4, hkv=1, d=64, scale=0.125, out=FAKE, batch=1, pcap=64, dtype=B.TT_FP32,
+             odt=B.TT_FP32, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return tt.lib().tt_block_attn_varlen(a["q"], a["k_ctx"], a["v_ctx"], a["lens"], a["pmax"],
+                                         a["k_blk"], a["v_blk"], a["L"], a["hq"], a["hkv"], a["d"],
+                                         a["scale"], a["out"], a["batch"], a["pcap"], a["dtype"],
+                                         a["odt"], a["ws"], a["wsb"], None, None)
+
+
+@pytest.mark.parametrize("kw", [dict(lens=None), dict(pmax=-1), dict(pmax=65), dict(q=None),
+                                dict(hq=3, hkv=2), dict(scale=float("nan"))])
+def test_varlen_rejects_invalid(kw):
+    assert varlen_call(**kw) == B.TT_EINVAL
+
+
+def test_varlen_empty_batch_and_workspace_query():
+    assert varlen_call(batch=0, lens=None) == B.TT_OK
+    assert tt.attn_workspace_bytes(8, 2048, 32, 32, 2, 128, torch.bfloat16) >= 0
+
+
+def multiblock_call(**kw):
+    a = dict(q=FAKE, k_ctx=FAKE, v_ctx=FAKE, kn=FAKE, vn=FAKE, S=16, N=4, hq=4, hkv=1, d=64,
+             scale=0.125, out=FAKE, batch=1, cap=48, dtype=B.TT_FP32, odt=B.TT_FP32, ws=FAKE,
+             wsb=1 << 30)
+    a.update(kw)
+    return tt.lib().tt_block_attn_multiblock(a["q"], a["k_ctx"], a["v_ctx"], a["kn"], a["vn"],
+                                             a["S"], a["N"], a["hq"], a["hkv"], a["d"], a["scale"],
+                                             a["out"], a["batch"], a["cap"], a["dtype"], a["odt"],
+                                             a["ws"], a["wsb"], None, None)
+
+
+@pytest.mark.parametrize("kw", [dict(cap=47), dict(kn=None), dict(vn=None), dict(out=None),
+                                dict(k_ctx=None), dict(N=-1), dict(S=-2), dict(hq=0),
+                                dict(dtype=B.TT_FP32, odt=B.TT_BF16)])
+def test_multiblock_rejects_invalid(kw):
+    assert multiblock_call(**kw) == B.TT_EINVAL
+
+
+def test_multiblock_empty_and_workspace_query():
+    assert multiblock_call(N=0, q=None, kn=None, vn=None, out=None, cap=0) == B.TT_OK
+    assert multiblock_call(batch=0) == B.TT_OK
+    assert multiblock_call(S=0) == B.TT_OK
+    n = tt.attn_multiblock_workspace_bytes(1, 256, 32, 32, 2, 128, torch.bfloat16)
+    assert n >= 0
+    with pytest.raises(ValueError):
+        tt.attn_multiblock_workspace_bytes(1, -1, 4, 32, 2, 128, torch.bfloat16)
+
+
 SELECT_BAD = [
     dict(mode="top_k", k=-1),
     dict(mode="leftmost", k=-3),

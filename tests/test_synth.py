@@ -65,3 +65,26 @@ def test_injected_ties():
     mx = x.max(-1, keepdims=True)
     n_max = (x == mx).sum(-1)
     assert (n_max >= 2).sum() == round(0.05 * 4 * 64)
+
+
+def test_varlen_inputs_lengths_and_garbage():
+    cfg = synth.get_config("decode_b8_p2048_l32")
+    a = synth.varlen_inputs(cfg, seed=3, batch=6, max_prefix_len=90, prefix_cap=96)
+    b = synth.varlen_inputs(cfg, seed=3, batch=6, max_prefix_len=90, prefix_cap=96)
+    lens = a["prefix_lens"]
+    assert np.array_equal(lens, b["prefix_lens"]) and lens.dtype == np.int32
+    assert lens.min() == 0 and lens.max() == 90 and np.all((lens >= 0) & (lens <= 90))
+    for bi, p in enumerate(lens):
+        kc = synth.f32_from_bf16_bits(a["k_ctx"][bi])
+        assert np.all(np.abs(kc[:, p:]) > 0.99 * synth.GARBAGE)   # bf16-rounded
+        assert np.all(np.abs(kc[:, :p]) < 100)
+
+
+def test_multiblock_inputs_shapes_and_hidden_rows():
+    cfg = synth.get_config("decode_b8_p2048_l32")
+    m = synth.multiblock_inputs(cfg, n_blocks=3, block_size=16, seed=1, batch=2)
+    assert m["q"].shape == (2, 32, 48, 128) and m["k_noisy"].shape == (2, 2, 48, 128)
+    kc = synth.f32_from_bf16_bits(m["k_ctx"])
+    assert np.all(np.abs(kc[:, :, 32:]) > 0.99 * synth.GARBAGE) and np.all(np.abs(kc[:, :, :32]) < 100)
+    m2 = synth.multiblock_inputs(cfg, n_blocks=3, block_size=16, seed=1, batch=2)
+    assert all(np.array_equal(m[k], m2[k]) for k in ("q", "k_ctx", "v_noisy"))
