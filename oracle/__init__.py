@@ -23,6 +23,9 @@ taken are stated next to each function.
   distribution p_theta).
 * ``unmask_step``  -- TwoTower paper §2.2 "Sampling" and Algorithm 2
   (ConfidenceSample), in its fixed-k reading (threshold switched off).
+* ``lmhead_unmask_step`` -- the unmask step fed by the LM-head projection of
+  the masked positions' hidden states (logits = hidden . W^T), §2.2
+  "Sampling" / Algorithm 2 (p_theta of DenoiserTower).
 * ``unmask_step_select`` -- the same step under the other selection rules of
   §2.2 "Sampling": Algorithm 2's threshold gamma with its T-r+1 deadline, the
   predict-and-noise sampler with the linear schedule alpha_t = 1 - t, and the
@@ -34,9 +37,10 @@ brute force in 50-digit arithmetic, closed forms, invariants and library
 routines (tests/test_oracle_*.py).  No function is "parity unpinned".
 """
 from .block_attn import block_attn, block_attn_multiblock, block_attn_varlen, decode_bf16
+from .lmhead import lmhead_logits, lmhead_unmask_step
 from .unmask import (LEFTMOST, SCHEDULE, THRESHOLD, TOP_K, commit_count, select_step, topk_select,
                      unmask_step, unmask_step_select, vocab_stats)
 
 __all__ = ["block_attn", "block_attn_varlen", "block_attn_multiblock", "decode_bf16", "vocab_stats", "unmask_step", "topk_select",
            "unmask_step_select", "select_step", "commit_count", "TOP_K", "THRESHOLD", "SCHEDULE",
-           "LEFTMOST"]
+           "LEFTMOST", "lmhead_logits", "lmhead_unmask_step"]
