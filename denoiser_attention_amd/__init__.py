@@ -9,10 +9,12 @@ synthetic-input generator (``synth``).
     block_attn_multiblock(q, k_ctx, v_ctx, k_noisy, v_noisy, S, scale) -> out (all noisy blocks)
     unmask_step(logits, mask_state, k, tokens)                     -> (tokens, mask_out)
     unmask_step_ex(logits, mask_state, select_rule(...), tokens)   -> (tokens, mask_out)
+    lmhead_unmask_step(hidden, weight, mask_state, select, tokens) -> (tokens, mask_out)
 """
 from ._binding import (  # noqa: F401
     LIB_PATH, SELECT_MODES, Prepared, Select, TTError, attn_multiblock_workspace_bytes,
     attn_workspace_bytes, block_attn, block_attn_multiblock, block_attn_varlen, lib,
+    lmhead_unmask_step, lmhead_unmask_workspace_bytes, prepare_lmhead_unmask_step,
     prepare_block_attn, prepare_unmask_commit, prepare_unmask_commit_ex, prepare_unmask_reduce,
     select_rule, status_string, unmask_commit, unmask_commit_ex, unmask_reduce, unmask_step,
     unmask_step_ex, unmask_workspace_bytes, version,
@@ -20,7 +22,8 @@ from ._binding import (  # noqa: F401
 
 __all__ = [
     "LIB_PATH", "SELECT_MODES", "Prepared", "Select", "TTError", "attn_multiblock_workspace_bytes",
-    "attn_workspace_bytes", "block_attn", "block_attn_multiblock", "block_attn_varlen", "lib", "prepare_block_attn", "prepare_unmask_commit", "prepare_unmask_commit_ex",
+    "attn_workspace_bytes", "block_attn", "block_attn_multiblock", "block_attn_varlen",
+    "lmhead_unmask_step", "lmhead_unmask_workspace_bytes", "prepare_lmhead_unmask_step", "lib", "prepare_block_attn", "prepare_unmask_commit", "prepare_unmask_commit_ex",
     "prepare_unmask_reduce", "select_rule", "status_string", "unmask_commit", "unmask_commit_ex",
     "unmask_reduce", "unmask_step", "unmask_step_ex", "unmask_workspace_bytes", "version",
 ]

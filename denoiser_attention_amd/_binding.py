@@ -70,6 +70,9 @@ _SIGNATURES = {
                                                        ctypes.POINTER(AttnOpts)]),
     "tt_block_attn_multiblock": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _i,
                                       _i, _i, _i, _vp, _sz, _vp, ctypes.POINTER(AttnOpts)]),
+    "tt_lmhead_unmask_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "tt_lmhead_unmask_step": (_i, [_vp, _vp, _vp, ctypes.POINTER(Select), _vp, _vp, _i, _i, _i, _i,
+                                   _vp, _vp, _vp, _sz, _vp]),
     "tt_unmask_workspace_bytes": (_sz, [_i, _i, _i]),
     "tt_unmask_step": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "tt_unmask_reduce": (_i, [_vp, _vp, _i, _i, _i, _vp, _sz, _vp]),
@@ -463,3 +466,52 @@ def prepare_unmask_commit_ex(mask_state, select: Select, tokens, mask_out, vocab
             _stream(device, stream))
     return Prepared(lib().tt_unmask_commit_ex, args, "tt_unmask_commit_ex",
                     (mask_state, tokens, mask_out, workspace, conf_out, pred_out, sel))
+
+
+def lmhead_unmask_workspace_bytes(batch, block_len, vocab, d_model) -> int:
+    n = lib().tt_lmhead_unmask_workspace_bytes(batch, block_len, vocab, d_model)
+    if n == SIZE_MAX:
+        raise ValueError("invalid or unsupported LM-head unmask shape")
+    return n
+
+
+def _lmhead_args(hidden, weight, mask_state, select, tokens, mask_out, conf_out, pred_out,
+                 workspace, stream):
+    device, B, L = _unmask_checks(None, mask_state, tokens, mask_out, conf_out, pred_out)
+    for name, t in (("hidden", hidden), ("weight", weight)):
+        _cuda_contig(name, t, device)
+        _require(t.dtype == torch.bfloat16 and t.dim() == (3 if name == "hidden" else 2),
+                 f"{name}: bfloat16")
+    _require(tuple(hidden.shape[:2]) == (B, L), "hidden: [B, L, d_model]")
+    V, d = weight.shape
+    _require(hidden.shape[2] == d, "weight: [vocab, d_model] with the hidden width")
+    if mask_out is None:
+        mask_out = torch.empty_like(mask_state)
+    need = lmhead_unmask_workspace_bytes(B, L, V, d)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    sel = Select(select.mode, select.k, select.gamma, select.steps_left, select.step,
+                 select.n_steps)
+    args = (_ptr(hidden), _ptr(weight), _ptr(mask_state), ctypes.byref(sel), _ptr(tokens),
+            _ptr(mask_out), B, L, V, d, _ptr(conf_out), _ptr(pred_out), _ptr(workspace), ws_bytes,
+            _stream(device, stream))
+    return args, mask_out, (hidden, weight, mask_state, tokens, mask_out, conf_out, pred_out,
+                            workspace, sel)
+
+
+def lmhead_unmask_step(hidden, weight, mask_state, select: Select, tokens, *, mask_out=None,
+                       conf_out=None, pred_out=None, workspace=None, stream=None):
+    """Unmask step with the LM-head projection fused in (tt_lmhead_unmask_step).
+    hidden [B, L, d] and weight [V, d] bfloat16; returns (tokens, mask_out)."""
+    args, mask_out, keep = _lmhead_args(hidden, weight, mask_state, select, tokens, mask_out,
+                                        conf_out, pred_out, workspace, stream)
+    _check(lib().tt_lmhead_unmask_step(*args), "tt_lmhead_unmask_step")
+    return tokens, mask_out
+
+
+def prepare_lmhead_unmask_step(hidden, weight, mask_state, select: Select, tokens, mask_out, *,
+                               conf_out=None, pred_out=None, workspace=None, stream=None):
+    args, mask_out, keep = _lmhead_args(hidden, weight, mask_state, select, tokens, mask_out,
+                                        conf_out, pred_out, workspace, stream)
+    return Prepared(lib().tt_lmhead_unmask_step, args, "tt_lmhead_unmask_step", keep)

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtt.so")
 
-SOURCES = ["tt_api.cpp", "attn_mfma.hip", "attn_shuffle.hip", "unmask.hip"]
+SOURCES = ["tt_api.cpp", "attn_mfma.hip", "attn_shuffle.hip", "unmask.hip", "lmhead.hip"]
 ARCH = "gfx950"
 
 COMMON = [

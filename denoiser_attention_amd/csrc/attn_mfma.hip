@@ -82,15 +82,6 @@ struct Lay {
   __device__ static int fv(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
-__device__ __forceinline__ int xcd_remap(int i, int n) {
-  // Workgroups are dispatched round-robin over the 8 XCDs.  Map them so that
-  // XCD x receives a contiguous range of logical ids.
-  const int xcd = i & 7, local = i >> 3;
-  const int per = (n + 7) >> 3;
-  const int tall = ((n & 7) == 0) ? 8 : (n & 7);
-  return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
-}
-
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -1,0 +1,335 @@
+// Fused LM-head projection and vocabulary statistics of the unmask step.
+//
+// Operation: TwoTower paper §2.2 "Sampling" / Algorithm 2.  The denoiser's
+// distribution at a still-masked position is the softmax of the logits its
+// LM head forms from the position's hidden state, logits = hidden . W^T with W
+// the [vocab, d_model] projection.  The unmask step needs, per masked
+// position, only (max logit, lowest id attaining it, sum of exp(logit - max)),
+// so the projection is fused with that reduction and the logits never leave
+// the chip.
+//
+// Kernels
+//   lmhead_rows_kernel   -- one workgroup: the masked positions, in order,
+//                           and their count (committed positions are never
+//                           projected).
+//   lmhead_stats_kernel  -- one workgroup per (128 masked rows, 256-entry
+//                           vocabulary slice).  Computes S^T = W_slice . H^T
+//                           with v_mfma_f32_32x32x16_bf16 (A = 32 vocabulary
+//                           rows, B = 32 hidden rows, both read as 16-byte
+//                           runs along d_model), so that in the accumulator
+//                           layout each lane owns one hidden row and 16 of a
+//                           tile's 32 vocabulary entries: the per-row
+//                           statistics are formed inside the lane, then with
+//                           lane ^ 32, then across the 4 waves through LDS.
+//                           Wave w covers vocabulary entries 64w..64w+63 of
+//                           the slice against all 128 rows (8 accumulator
+//                           tiles).  W and H tiles of 32 d_model columns
+//                           stream into a 6-stage LDS ring with 16-byte
+//                           direct-to-LDS loads (rows XOR-swizzled at 16-byte
+//                           granularity); 5 stages are in flight while one is
+//                           consumed.
+//   lmhead_merge_kernel  -- one wavefront per masked row: merges the row's
+//                           slice partials into one.
+// The confidence-ranking and commit step then runs on the merged partials.
+#include <climits>
+
+#include "tt_internal.h"
+
+namespace tt {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int NS = 6;                               // ring stages
+constexpr int ROWB = kLmK * 2;                      // bytes of one row of a stage (64)
+constexpr int W_TILE = kLmVocab * ROWB;             // 16 KB
+constexpr int H_TILE = kLmRows * ROWB;              // 8 KB
+constexpr int STAGE = W_TILE + H_TILE;              // 24 KB
+constexpr int W_LOADS = W_TILE / 16 / kThreads;     // 4 direct loads per thread
+constexpr int H_LOADS = H_TILE / 16 / kThreads;     // 2
+constexpr int PER_STAGE = W_LOADS + H_LOADS;        // vector-memory ops per stage
+static_assert(kLmVocab == 64 * kWaves, "one 64-entry vocabulary range per wave");
+static_assert(kLmRows == 128 && kLmK == 32, "tile shape");
+static_assert(NS * STAGE <= 160 * 1024, "ring fits the LDS");
+
+// Chunk q (16 bytes) of stage row r lives in slot q ^ f(r): eight consecutive
+// rows read at the same chunk then hit eight distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+
+struct Triple {
+  float m;
+  int arg;
+  float s;
+};
+
+__device__ __forceinline__ Triple combine(Triple a, Triple b) {
+  Triple r;
+  r.m = fmaxf(a.m, b.m);
+  const float sa = a.m == -INFINITY ? 0.0f : a.s * __builtin_amdgcn_exp2f((a.m - r.m) * kLog2e);
+  const float sb = b.m == -INFINITY ? 0.0f : b.s * __builtin_amdgcn_exp2f((b.m - r.m) * kLog2e);
+  r.s = sa + sb;
+  r.arg = a.m > b.m ? a.arg : (b.m > a.m ? b.arg : min(a.arg, b.arg));
+  return r;
+}
+
+__device__ __forceinline__ Triple shfl_xor_triple(Triple t, int mask) {
+  return Triple{__shfl_xor(t.m, mask), __shfl_xor(t.arg, mask), __shfl_xor(t.s, mask)};
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier that leaves outstanding loads in flight (unlike
+// __syncthreads, which also drains them).
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// One 16-byte direct-to-LDS load per lane from a wave-uniform base plus a
+// per-lane offset: lane i's bytes land at LDS address lds + 16*i.  Issued from
+// asm (no register outputs) so that the compiler does not drain it before
+// unrelated LDS reads; the explicit vmcnt waits and barriers order it.
+__device__ __forceinline__ void dma16_s(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ void wait_stages(int n_after) {
+  switch (n_after) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<PER_STAGE>(); break;
+    case 2: wait_vmcnt<2 * PER_STAGE>(); break;
+    case 3: wait_vmcnt<3 * PER_STAGE>(); break;
+    default: wait_vmcnt<4 * PER_STAGE>(); break;
+  }
+}
+static_assert(NS - 2 <= 4, "waits above cover NS - 2 stages in flight");
+
+__global__ __launch_bounds__(1024) void lmhead_rows_kernel(LmParams p) {
+  __shared__ int s_wave[16];
+  __shared__ int s_base;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_base = 0;
+  __syncthreads();
+  for (int i0 = 0; i0 < p.n_pos; i0 += 1024) {
+    const int i = i0 + tid;
+    const bool f = i < p.n_pos && p.mask_state[i] != 0;
+    const unsigned long long bal = __ballot(f);
+    const int below = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) s_wave[wave] = __popcll(bal);
+    __syncthreads();
+    int off = s_base;
+    for (int w = 0; w < wave; ++w) off += s_wave[w];
+    if (f) p.row_ids[off + below] = i;
+    __syncthreads();
+    if (tid == 0) {
+      int t = 0;
+      for (int w = 0; w < 16; ++w) t += s_wave[w];
+      s_base += t;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) *p.n_rows = s_base;
+}
+
+__global__ __launch_bounds__(kThreads, 1) void lmhead_stats_kernel(LmParams p, int n_rt) {
+  __shared__ __attribute__((aligned(1024))) char ring[NS * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int rt = logical % n_rt, slice = logical / n_rt;
+  const int n_rows = *p.n_rows;
+  const int row0 = rt * kLmRows;
+  if (row0 >= n_rows) return;                      // whole workgroup
+  const int rows_here = min(kLmRows, n_rows - row0);
+  const int vocab0 = slice * kLmVocab;
+  const int d = p.d;
+  const size_t rowb = (size_t)d * 2;
+
+  // Per-thread direct-load offsets (bytes from the stage's column base).
+  uint32_t woff[W_LOADS], hoff[H_LOADS];
+#pragma unroll
+  for (int j = 0; j < W_LOADS; ++j) {
+    const int i = tid + kThreads * j, r = i >> 2, q = i & 3;
+    const int v = min(vocab0 + r, p.V - 1);        // past the vocabulary: a valid row, masked later
+    woff[j] = (uint32_t)((size_t)(v - vocab0) * rowb) + ((q ^ swz(r)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < H_LOADS; ++j) {
+    const int i = tid + kThreads * j, r = i >> 2, q = i & 3;
+    const int row = p.row_ids[row0 + min(r, rows_here - 1)];
+    hoff[j] = (uint32_t)((size_t)row * rowb) + ((q ^ swz(r)) << 4);
+  }
+  const char* wbase = static_cast<const char*>(p.weight) + (size_t)vocab0 * rowb;
+  const char* hbase = static_cast<const char*>(p.hidden);
+  const uint32_t ring_u32 = (uint32_t)(uintptr_t)(lds_char*)ring;
+
+  auto issue = [&](int kt, int slot) {
+    const uint32_t st = ring_u32 + slot * STAGE;
+    const char* wk = wbase + (size_t)kt * ROWB;
+    const char* hk = hbase + (size_t)kt * ROWB;
+#pragma unroll
+    for (int j = 0; j < W_LOADS; ++j) dma16_s(wk, woff[j], st + (kThreads * j + wave * 64) * 16);
+#pragma unroll
+    for (int j = 0; j < H_LOADS; ++j)
+      dma16_s(hk, hoff[j], st + W_TILE + (kThreads * j + wave * 64) * 16);
+  };
+
+  // Operand rows of this lane: vocabulary rows 64*wave + 32*vt + (lane & 31),
+  // hidden rows 32*rt + (lane & 31); the lane half picks the 8-column run.
+  const int lr = lane & 31, hh = lane >> 5;
+  int a_row[2], b_row[4];
+#pragma unroll
+  for (int vt = 0; vt < 2; ++vt) a_row[vt] = 64 * wave + 32 * vt + lr;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) b_row[t] = 32 * t + lr;
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[vt][t] = f32x16{};
+
+  auto compute = [&](int slot) {
+    const char* st = ring + slot * STAGE;
+#pragma unroll
+    for (int s = 0; s < kLmK / 16; ++s) {
+      const int c = 2 * s + hh;
+      bf16x8 a[2], bq[4];
+#pragma unroll
+      for (int vt = 0; vt < 2; ++vt)
+        a[vt] = *reinterpret_cast<const bf16x8*>(st + a_row[vt] * ROWB + ((c ^ swz(a_row[vt])) << 4));
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        bq[t] = *reinterpret_cast<const bf16x8*>(st + W_TILE + b_row[t] * ROWB +
+                                                 ((c ^ swz(b_row[t])) << 4));
+#pragma unroll
+      for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[vt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[vt], bq[t], acc[vt][t], 0, 0, 0);
+    }
+  };
+
+  // Ring: stage i is refilled with column tile i + NS - 1 right after the
+  // barrier of iteration i + 1, when every wave has finished with it.
+  const int nk = d / kLmK;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int i = 0; i < nk; ++i) {
+    wait_stages(min(NS - 2, nk - 1 - i));
+    barrier();
+    if (i + NS - 1 < nk) issue(i + NS - 1, (i + NS - 1) % NS);
+    compute(i % NS);
+  }
+
+  // Statistics of each hidden row over this wave's 64 entries.  Accumulator
+  // register r of tile (vt, t) holds entry 64*wave + 32*vt + 8*(r/4) +
+  // 4*hh + r%4 of row 32*t + lr; they are visited in increasing id order, so
+  // a strict '>' keeps the lowest id among equal maxima.
+  Triple tr[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float m = -INFINITY;
+    int arg = INT_MAX;
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = vocab0 + 64 * wave + 32 * vt + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (v < p.V && acc[vt][t][r] > m) {
+          m = acc[vt][t][r];
+          arg = v;
+        }
+      }
+    float s = 0.0f;
+    if (m != -INFINITY) {
+      const float mb = m * kLog2e;
+#pragma unroll
+      for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = vocab0 + 64 * wave + 32 * vt + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (v < p.V) s += __builtin_amdgcn_exp2f(fmaf(acc[vt][t][r], kLog2e, -mb));
+        }
+    }
+    tr[t] = combine(Triple{m, arg, s}, shfl_xor_triple(Triple{m, arg, s}, 32));
+  }
+
+  // Across the 4 waves (LDS; the ring is free once every wave is past it).
+  barrier();
+  Triple* xt = reinterpret_cast<Triple*>(ring);   // [wave][128 rows]
+  if (hh == 0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) xt[wave * kLmRows + 32 * t + lr] = tr[t];
+  }
+  __syncthreads();
+  if (tid < rows_here) {
+    Triple r = xt[tid];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = combine(r, xt[w * kLmRows + tid]);
+    const int row = p.row_ids[row0 + tid];
+    VocabPartial out;
+    out.m = r.m;
+    out.arg = r.arg;
+    out.s = r.s;
+    out.pad = 0;
+    p.slices[(size_t)row * p.n_slices + slice] = out;
+  }
+}
+
+// One wavefront per masked row: lane i merges slices i, i+64, ..., then the
+// wavefront combines (max and lowest argmax do not depend on the order; the
+// sum is formed in one fixed order).
+constexpr int kMergeBatch = 8;
+
+__global__ __launch_bounds__(64) void lmhead_merge_kernel(LmParams p) {
+  const int i = blockIdx.x;
+  if (i >= *p.n_rows) return;
+  const int lane = threadIdx.x;
+  const int row = p.row_ids[i];
+  const VocabPartial* src = p.slices + (size_t)row * p.n_slices;
+  Triple t{-INFINITY, INT_MAX, 0.0f};
+  for (int c0 = 0; c0 < p.n_slices; c0 += 64 * kMergeBatch) {
+    VocabPartial q[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int c = c0 + 64 * j + lane;
+      if (c < p.n_slices) q[j] = src[c];
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j)
+      if (c0 + 64 * j + lane < p.n_slices) t = combine(t, Triple{q[j].m, q[j].arg, q[j].s});
+  }
+#pragma unroll
+  for (int mask = 32; mask >= 1; mask >>= 1) t = combine(t, shfl_xor_triple(t, mask));
+  if (lane == 0) {
+    VocabPartial out;
+    out.m = t.m;
+    out.arg = t.arg;
+    out.s = t.s;
+    out.pad = 0;
+    p.merged[row] = out;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_lmhead(const LmParams& p, hipStream_t stream) {
+  if (p.n_pos <= 0 || p.d % kLmK != 0 || p.d <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lmhead_rows_kernel, dim3(1), dim3(1024), 0, stream, p);
+  const long long n_rt = (p.n_pos + kLmRows - 1) / kLmRows;
+  const long long n = n_rt * p.n_slices;
+  if (n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(lmhead_stats_kernel, dim3((unsigned)n), dim3(kThreads), 0, stream, p,
+                     (int)n_rt);
+  hipLaunchKernelGGL(lmhead_merge_kernel, dim3((unsigned)p.n_pos), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace tt

@@ -478,3 +478,90 @@ TT_EXPORT tt_status tt_unmask_step_ex(const float* logits, const uint8_t* mask_s
   return unmask_run(logits, mask_state, select, tokens_out, mask_out, batch, block_len, vocab,
                     conf_out, pred_out, workspace, workspace_bytes, stream, true);
 }
+
+namespace {
+
+struct LmPlan {
+  int n_slices = 0;
+  size_t slices_off = 0, merged_off = 0, rows_off = 0, count_off = 0, ws_bytes = 0;
+  bool empty = false;
+};
+
+tt_status plan_lmhead(int B, int L, int V, int d, LmPlan* plan) {
+  if (B < 0 || L < 0 || V < 1 || d < 1) return TT_EINVAL;
+  if (L > tt::kUnmaskMaxL) return TT_EUNSUPPORTED;
+  if (d % tt::kLmK != 0) return TT_EUNSUPPORTED;
+  const long long n_pos = (long long)B * L;
+  if (n_pos > INT_MAX / 2) return TT_EUNSUPPORTED;
+  // 32-bit byte offsets inside the hidden matrix and a weight slice.
+  if (n_pos * d * 2 >= (1ll << 32) || (long long)tt::kLmVocab * d * 2 >= (1ll << 32))
+    return TT_EUNSUPPORTED;
+  plan->empty = n_pos == 0;
+  plan->n_slices = (int)cdiv(V, tt::kLmVocab);
+  if (plan->empty) return TT_OK;
+  size_t off = 0;
+  plan->slices_off = off;
+  off += align_up((size_t)n_pos * plan->n_slices * sizeof(tt::VocabPartial));
+  plan->merged_off = off;
+  off += align_up((size_t)n_pos * sizeof(tt::VocabPartial));
+  plan->rows_off = off;
+  off += align_up((size_t)n_pos * sizeof(int32_t));
+  plan->count_off = off;
+  off += align_up(sizeof(int32_t));
+  plan->ws_bytes = off;
+  return TT_OK;
+}
+
+}  // namespace
+
+TT_EXPORT size_t tt_lmhead_unmask_workspace_bytes(int batch, int block_len, int vocab,
+                                                  int d_model) {
+  LmPlan plan;
+  if (plan_lmhead(batch, block_len, vocab, d_model, &plan) != TT_OK) return SIZE_MAX;
+  return plan.ws_bytes;
+}
+
+TT_EXPORT tt_status tt_lmhead_unmask_step(const void* hidden, const void* weight,
+                                          const uint8_t* mask_state, const tt_select* select,
+                                          int32_t* tokens_out, uint8_t* mask_out, int batch,
+                                          int block_len, int vocab, int d_model,
+                                          float* conf_out, int32_t* pred_out, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+  UnmaskParams up{};
+  tt_status st = set_select(select, &up);
+  if (st != TT_OK) return st;
+  LmPlan plan;
+  st = plan_lmhead(batch, block_len, vocab, d_model, &plan);
+  if (st != TT_OK || plan.empty) return st;
+  if (!hidden || !weight || !mask_state || !tokens_out || !mask_out) return TT_EINVAL;
+  if (!workspace || workspace_bytes < plan.ws_bytes) return TT_EINVAL;
+  st = device_present();
+  if (st != TT_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  tt::LmParams lp{};
+  lp.hidden = hidden;
+  lp.weight = weight;
+  lp.mask_state = mask_state;
+  lp.slices = reinterpret_cast<tt::VocabPartial*>(ws + plan.slices_off);
+  lp.merged = reinterpret_cast<tt::VocabPartial*>(ws + plan.merged_off);
+  lp.row_ids = reinterpret_cast<int32_t*>(ws + plan.rows_off);
+  lp.n_rows = reinterpret_cast<int32_t*>(ws + plan.count_off);
+  lp.n_pos = batch * block_len;
+  lp.V = vocab;
+  lp.d = d_model;
+  lp.n_slices = plan.n_slices;
+  up.mask_state = mask_state;
+  up.partials = lp.merged;
+  up.B = batch;
+  up.L = block_len;
+  up.V = vocab;
+  up.n_chunks = 1;
+  up.tokens_out = tokens_out;
+  up.mask_out = mask_out;
+  up.conf_out = conf_out;
+  up.pred_out = pred_out;
+  (void)hipGetLastError();
+  const hipError_t e = tt::launch_lmhead(lp, stream);
+  if (e != hipSuccess) return TT_EHIP;
+  return to_status(tt::launch_topk_commit(up, stream));
+}

@@ -104,6 +104,16 @@ hipError_t launch_attn_mfma(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_shuffle(const AttnParams& p, int in_bf16, hipStream_t stream);
 hipError_t launch_attn_merge(const AttnParams& p, hipStream_t stream);
 
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Map dispatch index i of n to a logical index such that XCD x receives
+// a contiguous range of logical ids.
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+  const int xcd = i & 7, local = i >> 3;
+  const int per = (n + 7) >> 3;
+  const int tall = ((n & 7) == 0) ? 8 : (n & 7);
+  return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+}
+
 // Per-chunk partial of the vocabulary pass for one masked row.
 struct VocabPartial {
   float m;        // max logit in the chunk
@@ -133,5 +143,22 @@ enum { kSelTopK = 0, kSelThreshold = 1, kSelSchedule = 2, kSelLeftmost = 3 };
 
 hipError_t launch_vocab_reduce(const UnmaskParams& p, hipStream_t stream);
 hipError_t launch_topk_commit(const UnmaskParams& p, hipStream_t stream);
+
+// Fused LM-head projection + vocabulary statistics.
+constexpr int kLmRows = 128;     // hidden rows per workgroup
+constexpr int kLmVocab = 256;    // vocabulary entries per workgroup (one slice)
+constexpr int kLmK = 32;         // d_model per pipeline stage
+struct LmParams {
+  const void* hidden;        // [B*L, d] bf16
+  const void* weight;        // [V, d] bf16
+  const uint8_t* mask_state; // [B*L]
+  int32_t* row_ids;          // [B*L] masked rows in order (workspace)
+  int32_t* n_rows;           // [1] their count (workspace)
+  VocabPartial* slices;      // [B*L, n_slices] per-slice partials (workspace)
+  VocabPartial* merged;      // [B*L] one partial per masked row (workspace)
+  int n_pos;                 // B*L
+  int V, d, n_slices;
+};
+hipError_t launch_lmhead(const LmParams& p, hipStream_t stream);
 
 }  // namespace tt

@@ -151,7 +151,7 @@ def _rng(seed: int, cfg: Config, tensor_id: int, step: int) -> np.random.Generat
 
 # tensor ids for seed derivation
 _T_Q, _T_KCTX, _T_VCTX, _T_KBLK, _T_VBLK, _T_OUTLIER, _T_LOGITS, _T_PLANT, _T_TIE, \
-    _T_GARBAGE, _T_LENS = range(11)
+    _T_GARBAGE, _T_LENS, _T_HIDDEN, _T_WEIGHT, _T_HPLANT = range(14)
 
 
 def attn_inputs(cfg: Config, seed: int = 0, step: int = 0, prefix_len: int | None = None,
@@ -295,3 +295,38 @@ def multiblock_inputs(cfg: Config, n_blocks: int, block_size: int, seed: int = 0
     out.update(n_blocks=n_blocks, block_size=block_size, batch=B, scale=cfg.softmax_scale,
                dtype=cfg.dtype)
     return out
+
+
+# Hidden width of the synthetic LM head (the pages give none).
+LM_D_MODEL = 2688
+
+
+def lmhead_inputs(cfg: Config, d_model: int = LM_D_MODEL, seed: int = 0, step: int = 0,
+                  batch: int | None = None, block_len: int | None = None,
+                  vocab: int | None = None, plant_frac: float = 0.25) -> dict:
+    """Final hidden states and an LM-head weight for the fused projection +
+    unmask step, as bf16 bit patterns.
+
+    hidden [B, L, d] ~ N(0, 1); weight [V, d] ~ N(0, logit_std / sqrt(d)), so
+    the logits are about N(0, logit_std).  A seeded fraction of the positions
+    (plant_frac) get a hidden state that is a scaled copy of one seeded
+    weight row, which makes that id a confident prediction (the same weights
+    serve every step).  Returns dict(hidden, weight, d_model, planted)."""
+    B = cfg.batch if batch is None else batch
+    L = cfg.block_len if block_len is None else block_len
+    V = cfg.vocab if vocab is None else vocab
+    r_w = _rng(seed, cfg, _T_WEIGHT, 0)
+    w = r_w.standard_normal((V, d_model), dtype=np.float32) * np.float32(cfg.logit_std / np.sqrt(d_model))
+    h = _rng(seed, cfg, _T_HIDDEN, step).standard_normal((B, L, d_model), dtype=np.float32)
+    r = _rng(seed, cfg, _T_HPLANT, step)
+    n_plant = int(round(plant_frac * B * L))
+    planted = []
+    if n_plant > 0:
+        flat = r.choice(B * L, size=n_plant, replace=False)
+        ids = r.integers(0, V, size=n_plant)
+        for f, v in zip(flat, ids):
+            b, l = divmod(int(f), L)
+            h[b, l] = w[v] * np.float32(1.5 * np.sqrt(d_model) / cfg.logit_std)
+            planted.append((b, l, int(v)))
+    return dict(hidden=bf16_bits_from_f32(h), weight=bf16_bits_from_f32(w), d_model=d_model,
+                planted=planted)

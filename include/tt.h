@@ -273,6 +273,36 @@ tt_status tt_unmask_commit_ex(const uint8_t* mask_state, const tt_select* select
                               int vocab, float* conf_out, int32_t* pred_out,
                               const void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------ */
+/* Fused LM head + unmask: TwoTower paper §2.2 "Sampling", Algorithm 2.       */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of workspace tt_lmhead_unmask_step needs (SIZE_MAX for invalid or
+ * unsupported sizes). */
+size_t tt_lmhead_unmask_workspace_bytes(int batch, int block_len, int vocab, int d_model);
+
+/* One unmasking step whose logits come from the denoiser's LM head, without
+ * writing them to memory: for every still-masked position,
+ *   logits[v] = sum_i hidden[b,l,i] * weight[v,i]      (bf16 inputs, fp32 sums)
+ * and then pred, conf and the selection exactly as tt_unmask_step_ex does on
+ * those logits.  The hidden rows of positions that are not masked are never
+ * read.
+ *   hidden      [batch, block_len, d_model]  bf16
+ *   weight      [vocab, d_model]             bf16 (the projection, one row per id)
+ *   d_model     a positive multiple of 32 (otherwise TT_EUNSUPPORTED); also
+ *               batch*block_len*d_model*2 < 2^32
+ *   select, tokens_out, mask_out, conf_out, pred_out, batch, block_len
+ *   (<= 1024), vocab, workspace, stream: as for tt_unmask_step_ex.
+ * The logits are fp32 sums of d_model exact bf16 products, so pred, conf and
+ * the commit set can differ from an exact computation only where the top two
+ * logits, or two confidences at the selection boundary, are that close.
+ * The call is deterministic. */
+tt_status tt_lmhead_unmask_step(const void* hidden, const void* weight,
+                                const uint8_t* mask_state, const tt_select* select,
+                                int32_t* tokens_out, uint8_t* mask_out, int batch, int block_len,
+                                int vocab, int d_model, float* conf_out, int32_t* pred_out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }  /* extern "C" */
 #endif

@@ -224,6 +224,37 @@ def test_select_rule_struct_and_unknown_mode():
         tt.select_rule("greedy")
 
 
+def lmhead_call(**kw):
+    a = dict(h=FAKE, w=FAKE, m=FAKE, sel=tt.select_rule("top_k", k=2), tok=FAKE, mo=FAKE, B=2,
+             L=16, V=1000, d=64, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    sel = None if a["sel"] is None else ctypes.byref(a["sel"])
+    return tt.lib().tt_lmhead_unmask_step(a["h"], a["w"], a["m"], sel, a["tok"], a["mo"], a["B"],
+                                          a["L"], a["V"], a["d"], None, None, a["ws"], a["wsb"],
+                                          None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h=None), B.TT_EINVAL), (dict(w=None), B.TT_EINVAL), (dict(m=None), B.TT_EINVAL),
+    (dict(tok=None), B.TT_EINVAL), (dict(mo=None), B.TT_EINVAL), (dict(sel=None), B.TT_EINVAL),
+    (dict(ws=None), B.TT_EINVAL), (dict(wsb=100), B.TT_EINVAL), (dict(d=0), B.TT_EINVAL),
+    (dict(V=0), B.TT_EINVAL), (dict(d=48), B.TT_EUNSUPPORTED), (dict(L=1025), B.TT_EUNSUPPORTED),
+    (dict(B=1 << 16, L=1024, d=4096), B.TT_EUNSUPPORTED),
+    (dict(sel=tt.select_rule("threshold", gamma=0.5, steps_left=0)), B.TT_EINVAL),
+])
+def test_lmhead_rejects_invalid(kw, status):
+    assert lmhead_call(**kw) == status
+
+
+def test_lmhead_empty_and_workspace():
+    assert lmhead_call(B=0, h=None, w=None, m=None, tok=None, mo=None, ws=None, wsb=0) == B.TT_OK
+    n = tt.lmhead_unmask_workspace_bytes(8, 32, 131072, 2688)
+    # per-slice partials + merged partials + row list + count, each 256-byte aligned
+    assert n == 256 * 512 * 16 + 256 * 16 + 1024 + 256
+    with pytest.raises(ValueError):
+        tt.lmhead_unmask_workspace_bytes(8, 32, 131072, 100)
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "nope.so"))
