@@ -24,10 +24,10 @@
 //                           Wave w covers vocabulary entries 64w..64w+63 of
 //                           the slice against all 128 rows (8 accumulator
 //                           tiles).  W and H tiles of 32 d_model columns
-//                           stream into a 6-stage LDS ring with 16-byte
-//                           direct-to-LDS loads (rows XOR-swizzled at 16-byte
-//                           granularity); 5 stages are in flight while one is
-//                           consumed.
+//                           stream into a 3-stage LDS ring (72 KB, so two
+//                           workgroups share a CU) with 16-byte direct-to-LDS
+//                           loads (rows XOR-swizzled at 16-byte granularity);
+//                           2 stages are in flight while one is consumed.
 //   lmhead_merge_kernel  -- one wavefront per masked row: merges the row's
 //                           slice partials into one.
 // The confidence-ranking and commit step then runs on the merged partials.
@@ -45,7 +45,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int NS = 6;                               // ring stages
+constexpr int NS = 3;                               // ring stages (2 workgroups per CU)
 constexpr int ROWB = kLmK * 2;                      // bytes of one row of a stage (64)
 constexpr int W_TILE = kLmVocab * ROWB;             // 16 KB
 constexpr int H_TILE = kLmRows * ROWB;              // 8 KB
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(1024) void lmhead_rows_kernel(LmParams p) {
   if (tid == 0) *p.n_rows = s_base;
 }
 
-__global__ __launch_bounds__(kThreads, 1) void lmhead_stats_kernel(LmParams p, int n_rt) {
+__global__ __launch_bounds__(kThreads, 2) void lmhead_stats_kernel(LmParams p, int n_rt) {
   __shared__ __attribute__((aligned(1024))) char ring[NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
