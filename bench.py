@@ -8,11 +8,17 @@ still masked, the most logits to read).  Inputs are resident in HBM before
 timing starts; several independent input sets are rotated so that the working
 set exceeds the 256 MB Infinity Cache and every step streams from HBM.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--graph]
+
+The timed loop issues each step's three library calls on one stream.  With
+--graph each input set's step is captured once into a HIP graph and the loop
+replays the graphs instead (checked bit for bit against an eager step; on
+this stack the replays have measured slower than the eager calls).
 
 Prints ONE JSON line: block-tokens/s over the timed steps, the roofline of the
-dominant kernel (the vocabulary pass, HBM-bound) measured with HIP events on
-the launch stream, and the CPU oracle timed on the same host.
+dominant kernel (the vocabulary pass, HBM-bound; its duration from HIP events
+around a back-to-back loop of that kernel alone on the launch stream), the
+attention call measured the same way, and the CPU oracle timed on the host.
 """
 from __future__ import annotations
 
@@ -43,6 +49,10 @@ def parse_args():
     ap.add_argument("--prefix-len", type=int, default=None)
     ap.add_argument("--rotate", type=int, default=0, help="input sets rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one captured HIP graph per input set instead of eager calls")
+    ap.add_argument("--kernel-reps", type=int, default=200,
+                    help="back-to-back launches timed for the per-kernel roofline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     return ap.parse_args()
@@ -85,9 +95,10 @@ def recorded_traffic(workload: str):
     return float(m.group(1))
 
 
-def cpu_baseline(cfg, inp, logits0, mask):
-    """The oracle as it stands, on the host cores, over one full step of the
-    same workload (all heads of the attention call, all masked rows)."""
+def cpu_baseline(cfg, host_sets, mask, min_seconds=10.0):
+    """The oracle as it stands, on the host cores, over whole steps of the same
+    workload (all heads of the attention call, all masked rows), repeated over
+    the rotated input sets until about min_seconds have passed."""
     import threadpoolctl
 
     import oracle
@@ -95,21 +106,27 @@ def cpu_baseline(cfg, inp, logits0, mask):
             if i.get("user_api") == "blas"]
     threads = max(blas) if blas else 1
     f = lambda a: oracle.decode_bf16(a) if a.dtype == np.uint16 else a.astype(np.float64)
-    t0 = time.perf_counter()
-    oracle.block_attn(f(inp["q"]), f(inp["k_ctx"]), f(inp["v_ctx"]), inp["prefix_len"],
-                      f(inp["k_blk"]), f(inp["v_blk"]), inp["scale"])
-    t_attn = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.unmask_step(logits0, mask, cfg.k)
-    t_unmask = time.perf_counter() - t0
-    t_step = t_attn + t_unmask
+    t_attn = t_unmask = 0.0
+    steps = 0
+    while steps < len(host_sets) and (steps == 0 or t_attn + t_unmask < min_seconds):
+        inp, lg = host_sets[steps]
+        t0 = time.perf_counter()
+        oracle.block_attn(f(inp["q"]), f(inp["k_ctx"]), f(inp["v_ctx"]), inp["prefix_len"],
+                          f(inp["k_blk"]), f(inp["v_blk"]), inp["scale"])
+        t_attn += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.unmask_step(lg, mask, cfg.k)
+        t_unmask += time.perf_counter() - t0
+        steps += 1
+    t_step = (t_attn + t_unmask) / steps
     B, L = mask.shape
     return {
         "value": B * L / t_step, "unit": "block-tokens/s", "cores": threads, "kind": "oracle",
-        "sample": (f"one full step of {cfg.name}: attention over all {cfg.batch}x{cfg.n_q_heads} "
-                   f"(batch, head) pairs in numpy fp64 ({t_attn:.2f} s, BLAS threads={threads}), "
-                   f"unmask of all {int(mask.sum())} masked rows ({t_unmask:.2f} s, one thread)"),
-        "seconds": t_step,
+        "sample": (f"{steps} full steps of {cfg.name} (distinct input sets): attention over all "
+                   f"{cfg.batch}x{cfg.n_q_heads} (batch, head) pairs in numpy fp64 "
+                   f"({t_attn:.2f} s, BLAS threads={threads}), unmask of all {int(mask.sum())} "
+                   f"masked rows per step ({t_unmask:.2f} s, one thread)"),
+        "seconds": t_attn + t_unmask,
     }
 
 
@@ -155,17 +172,16 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     sets = []
-    host0 = None
+    host_sets = []
     for r in range(R):
         inp = synth.attn_inputs(cfg, seed=0, step=r)
         lg = synth.logits(cfg, seed=0, step=r)
-        if r == 0:
-            host0 = (inp, lg)
+        if r < 3 and not args.no_cpu_baseline:
+            host_sets.append((inp, lg))
         t = {n: up(inp[n]) for n in ("q", "k_ctx", "v_ctx", "k_blk", "v_blk")}
         t["logits"] = up(lg)
         sets.append(t)
-        if r:
-            del lg
+        del lg
     mask = torch.ones((B, L), dtype=torch.uint8, device=dev)
     mask_out = torch.empty_like(mask)
     tokens = torch.full((B, L), -1, dtype=torch.int32, device=dev)
@@ -174,48 +190,103 @@ def main():
     attn_ws_n = tt.attn_workspace_bytes(B, P, L, Hq, Hkv, D, dt)
     attn_ws = torch.empty(max(attn_ws_n, 1), dtype=torch.uint8, device=dev)
     um_ws = torch.empty(tt.unmask_workspace_bytes(B, L, V), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
+    # A stream of our own (default priority): the graphs are captured on it
+    # and every timed launch goes to it.
+    stream = torch.cuda.Stream(dev)
 
     # Validate every call once; a step then costs three ctypes calls on the host.
     calls = []
-    for t in sets:
-        calls.append((
-            tt.prepare_block_attn(t["q"], t["k_ctx"], t["v_ctx"], P, t["k_blk"], t["v_blk"],
-                                  cfg.softmax_scale, out, workspace=attn_ws if attn_ws_n else None,
-                                  stream=stream),
-            tt.prepare_unmask_reduce(t["logits"], mask, um_ws, stream=stream),
-            tt.prepare_unmask_commit(mask, cfg.k, tokens, mask_out, V, um_ws, stream=stream),
-        ))
-
-    def step(i, ev=None):
-        attn, reduce, commit = calls[i % R]
-        if ev is not None:
-            ev[0].record(stream)
-        attn()
-        if ev is not None:
-            ev[1].record(stream)
-        reduce()
-        if ev is not None:
-            ev[2].record(stream)
-        commit()
-
-    for i in range(args.warmup):
-        step(i)
+    with torch.cuda.stream(stream):
+        for t in sets:
+            calls.append((
+                tt.prepare_block_attn(t["q"], t["k_ctx"], t["v_ctx"], P, t["k_blk"], t["v_blk"],
+                                      cfg.softmax_scale, out,
+                                      workspace=attn_ws if attn_ws_n else None, stream=stream),
+                tt.prepare_unmask_reduce(t["logits"], mask, um_ws, stream=stream),
+                tt.prepare_unmask_commit(mask, cfg.k, tokens, mask_out, V, um_ws, stream=stream),
+            ))
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    def eager_step(i):
+        for c in calls[i % R]:
+            c()
+
+    graphs = None
+    if args.graph:
+        graphs = []
+        for i in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                eager_step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def step(i):
+        if graphs is None:
+            eager_step(i)
+        else:
+            graphs[i % R].replay()
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    torch.cuda.synchronize()
+
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i, evs[i])
-    t_end.record(stream)
+    with torch.cuda.stream(stream):
+        t_start.record(stream)
+        for i in range(args.steps):
+            step(i)
+        t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    attn_us = 1e3 * np.mean([e[0].elapsed_time(e[1]) for e in evs])
-    reduce_us = 1e3 * np.mean([e[1].elapsed_time(e[2]) for e in evs])
+
+    # Graph replays must reproduce an eager step bit for bit.
+    graph_check = None
+    if graphs is not None:
+        tokens.fill_(-1)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            eager_step(0)
+        torch.cuda.synchronize()
+        ref = (out.clone(), tokens.clone(), mask_out.clone())
+        for _ in range(2):
+            out.fill_(0)
+            tokens.fill_(-1)
+            mask_out.fill_(7)
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                graphs[0].replay()
+            torch.cuda.synchronize()
+            ok = (torch.equal(out.view(torch.int16), ref[0].view(torch.int16))
+                  and torch.equal(tokens, ref[1]) and torch.equal(mask_out, ref[2]))
+            if not ok:
+                print("bench.py: graph replay differs from the eager step", file=sys.stderr)
+                sys.exit(1)
+        graph_check = "graph replays == eager step (bitwise, 2 replays)"
+
+    def kernel_loop_us(which):
+        """Average duration of one launch of call `which` (0 attention, 1
+        vocabulary pass) over back-to-back launches on rotated input sets,
+        between two HIP events on the launch stream."""
+        n = args.kernel_reps
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            for i in range(5):
+                calls[i % R][which]()
+            e0.record(stream)
+            for i in range(n):
+                calls[i % R][which]()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / n
+
+    reduce_us = kernel_loop_us(1)
+    attn_us = kernel_loop_us(0)
 
     n_masked = B * L
     reduce_bytes = n_masked * V * 4 + B * L          # masked logit rows + mask bytes
@@ -250,6 +321,8 @@ def main():
             "traffic": recorded_traffic(cfg.name),
             "algorithmic_bytes_per_launch": reduce_bytes,
             "avg_launch_us": reduce_us,
+            "timing": f"HIP events around {args.kernel_reps} back-to-back launches on the "
+                      "launch stream",
         },
         "attention": {
             "avg_call_us": attn_us, "tflops": attn_tflops,
@@ -257,11 +330,12 @@ def main():
             "roof_us": attn_t_roof * 1e6, "roof_frac": attn_t_roof * 1e6 / attn_us,
             "algorithmic_bytes": attn_bytes, "flops": attn_flops,
         },
+        "step_launch": "HIP graph replay per step" if graphs is not None else "eager calls",
+        "graph_check": graph_check,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        inp0, lg0 = host0
-        result["cpu_baseline"] = cpu_baseline(cfg, inp0, lg0, np.ones((B, L), np.uint8))
+        result["cpu_baseline"] = cpu_baseline(cfg, host_sets, np.ones((B, L), np.uint8))
     print(json.dumps(result), flush=True)
 
 
