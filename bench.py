@@ -51,6 +51,10 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="replay one captured HIP graph per input set instead of eager calls")
+    ap.add_argument("--suite", action="store_true",
+                    help="instead of the step: one JSON line per supplementary workload "
+                         "(attention of every configuration, per-sequence prefixes, the "
+                         "multi-block pass, selection rules, the fused LM head)")
     ap.add_argument("--kernel-reps", type=int, default=200,
                     help="back-to-back launches timed for the per-kernel roofline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -130,6 +134,168 @@ def cpu_baseline(cfg, host_sets, mask, min_seconds=10.0):
     }
 
 
+def _roof(bytes_, flops):
+    t_hbm = bytes_ / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    return max(t_hbm, t_mfma), ("hbm" if t_hbm >= t_mfma else "mfma")
+
+
+def suite(args):
+    """Supplementary measurements, one JSON line each (not the headline)."""
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import denoiser_attention_amd as tt
+    from denoiser_attention_amd import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(dev)
+    reps = max(10, args.kernel_reps // 4)
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def time_calls(fns, n=reps):
+        """Average us per call over back-to-back calls (rotating fns), HIP events."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            for i in range(3):
+                fns[i % len(fns)]()
+            e0.record(stream)
+            for i in range(n):
+                fns[i % len(fns)]()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / n
+
+    def emit(name, us, bytes_, flops, **extra):
+        roof_s, bound = _roof(bytes_, flops)
+        line = {"suite": name, "avg_us": us, "bound": bound, "roof_us": roof_s * 1e6,
+                "roof_frac": roof_s * 1e6 / us, "GBps": bytes_ / us / 1e3,
+                "TFLOPs": flops / us / 1e6}
+        line.update(extra)
+        print(json.dumps(line), flush=True)
+
+    def n_rotate(set_bytes):
+        # Enough independent input sets that one pass over them exceeds 1 GB
+        # (four times the Infinity Cache), as in the step benchmark.
+        return int(min(48, max(2, np.ceil(1.0e9 / set_bytes))))
+
+    def attn_case(name, cfg, **kw):
+        B, Hq, Hkv, D, L = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_len
+        P = cfg.prefix_len if "prefix_len" not in kw else kw["prefix_len"]
+        n_sets = n_rotate(2 * (2 * B * Hq * L * D + 2 * B * Hkv * (P + L) * D))
+        fns, keep = [], []
+        for r in range(n_sets):
+            inp = synth.attn_inputs(cfg, seed=0, step=r, **kw)
+            t = {n: up(inp[n]) for n in ("q", "k_ctx", "v_ctx", "k_blk", "v_blk")}
+            out = torch.empty_like(t["q"])
+            with torch.cuda.stream(stream):
+                fns.append(tt.prepare_block_attn(t["q"], t["k_ctx"], t["v_ctx"], P, t["k_blk"],
+                                                 t["v_blk"], cfg.softmax_scale, out, stream=stream))
+            keep.append((t, out))
+        us = time_calls(fns)
+        s = 2
+        emit(name, us, s * (2 * B * Hq * L * D + 2 * B * Hkv * (P + L) * D),
+             4 * B * Hq * L * (P + L) * D, kind="attention", B=B, P=P, L=L, Hq=Hq, Hkv=Hkv, D=D,
+             input_sets=n_sets)
+        del keep, fns
+
+    # Attention at every configuration (bf16) and the prefix-bound shapes.
+    for name, kw in (("decode_b8_p2048_l32", {}), ("block256_b16_p1024", {}),
+                     ("gen8k_b4_l256", dict(prefix_len=512)), ("gen8k_b4_l256", dict(prefix_len=8192)),
+                     ("gen8k_b4_l256", dict(prefix_len=16128)), ("highbatch_b64_p4096_l64", {}),
+                     ("decode_l16", {}), ("decode_l1", {})):
+        cfg = synth.get_config(name, **kw)
+        attn_case(f"attn {name} P={cfg.prefix_len}", cfg)
+
+    # Per-sequence prefix lengths (decode geometry, lengths mixed in [0, 2048]).
+    cfg = synth.get_config("decode_b8_p2048_l32")
+    inp = synth.varlen_inputs(cfg, seed=0, max_prefix_len=2048)
+    t = {n: up(inp[n]) for n in ("q", "k_ctx", "v_ctx", "k_blk", "v_blk")}
+    lens = torch.from_numpy(inp["prefix_lens"]).to(dev)
+    out = torch.empty_like(t["q"])
+    fn = lambda: tt.block_attn_varlen(t["q"], t["k_ctx"], t["v_ctx"], lens, 2048, t["k_blk"],
+                                      t["v_blk"], cfg.softmax_scale, out=out, stream=stream)
+    us = time_calls([fn])
+    Ps = inp["prefix_lens"].astype(np.int64)
+    B, Hq, Hkv, D, L = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_len
+    emit("attn varlen decode_b8 lens=" + ",".join(map(str, Ps.tolist())), us,
+         2 * (2 * B * Hq * L * D + 2 * Hkv * int((Ps + L).sum()) * D),
+         4 * Hq * L * int((Ps + L).sum()) * D, kind="attention varlen")
+    del t, out
+
+    # Training-style pass over all noisy blocks: 8 and 32 blocks of 256.
+    for nb, bsz in ((8, 1), (32, 1)):
+        cfg = synth.get_config("block256_b16_p1024")
+        mb = synth.multiblock_inputs(cfg, nb, 256, seed=0, batch=bsz)
+        t = {n: up(mb[n]) for n in ("q", "k_ctx", "v_ctx", "k_noisy", "v_noisy")}
+        out = torch.empty_like(t["q"])
+        fn = lambda: tt.block_attn_multiblock(t["q"], t["k_ctx"], t["v_ctx"], t["k_noisy"],
+                                              t["v_noisy"], 256, cfg.softmax_scale, out=out,
+                                              stream=stream)
+        us = time_calls([fn], n=max(5, reps // 4))
+        Hq, Hkv, D, S = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, 256
+        keys = sum(j * S + S for j in range(nb))        # visible keys per query row, summed over blocks
+        emit(f"attn multiblock {nb}x256 batch={bsz}", us,
+             2 * bsz * (2 * Hq * nb * S * D + 2 * Hkv * (nb * S + (nb - 1) * S) * D),
+             4 * bsz * Hq * S * keys * D, kind="attention multiblock")
+        del t, out
+
+    # Vocabulary pass and the selection rules (decode workload, all positions masked).
+    cfg = synth.get_config("decode_b8_p2048_l32")
+    B, L, V = cfg.batch, cfg.block_len, cfg.vocab
+    n_sets = n_rotate(B * L * V * 4)
+    xs = [up(synth.logits(cfg, seed=0, step=r)) for r in range(n_sets)]
+    mask = torch.ones((B, L), dtype=torch.uint8, device=dev)
+    tok = torch.zeros((B, L), dtype=torch.int32, device=dev)
+    mo = torch.empty_like(mask)
+    ws = torch.empty(tt.unmask_workspace_bytes(B, L, V), dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(stream):
+        reds = [tt.prepare_unmask_reduce(x, mask, ws, stream=stream) for x in xs]
+        reds[0]()
+    emit("unmask reduce decode_b8", time_calls(reds), B * L * V * 4 + B * L, 0,
+         kind="vocabulary pass", input_sets=n_sets)
+    for mode, params in (("top_k", dict(k=8)), ("threshold", dict(gamma=0.8, steps_left=4)),
+                         ("schedule", dict(step=1, n_steps=4)), ("leftmost", dict(k=1))):
+        with torch.cuda.stream(stream):
+            c = tt.prepare_unmask_commit_ex(mask, tt.select_rule(mode, **params), tok, mo, V, ws,
+                                            stream=stream)
+        emit(f"unmask commit {mode} decode_b8", time_calls([c]), B * L * 16 * 16 + 2 * B * L, 0,
+             kind="selection")
+    del xs, reds
+
+    # Fused LM head + unmask vs the library GEMM + this unmask.
+    d = synth.LM_D_MODEL
+    for name, B, L in (("decode_b8", 8, 32), ("block256_b16", 16, 256)):
+        V = 131072
+        torch.manual_seed(0)
+        h = torch.randn(B, L, d, device=dev).to(torch.bfloat16)
+        w = (torch.randn(V, d, device=dev) * (3.0 / d ** 0.5)).to(torch.bfloat16)
+        mask = torch.ones((B, L), dtype=torch.uint8, device=dev)
+        tok = torch.zeros((B, L), dtype=torch.int32, device=dev)
+        mo = torch.empty_like(mask)
+        with torch.cuda.stream(stream):
+            call = tt.prepare_lmhead_unmask_step(h, w, mask, tt.select_rule("top_k", k=8), tok, mo,
+                                                 stream=stream)
+        us = time_calls([call], n=10)
+        rows = B * L
+        logits = torch.empty((rows, V), dtype=torch.float32, device=dev)
+        ws = torch.empty(tt.unmask_workspace_bytes(B, L, V), dtype=torch.uint8, device=dev)
+
+        def unfused():
+            logits.copy_(torch.matmul(h.view(rows, d), w.t()))
+            tt.unmask_step(logits.view(B, L, V), mask, 8, tok, mask_out=mo, workspace=ws,
+                           stream=stream)
+        us_u = time_calls([unfused], n=10)
+        emit(f"lmhead+unmask {name} rows={rows} V={V} d={d}", us, V * d * 2 + rows * d * 2,
+             2.0 * rows * V * d, kind="fused LM head", unfused_library_gemm_us=us_u)
+        del h, w, logits
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -140,6 +306,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.suite:
+        suite(args)
         return
 
     import torch
