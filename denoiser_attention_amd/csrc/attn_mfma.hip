@@ -292,12 +292,20 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     return sacc;
   };
 
-  // Online softmax of tile t's scores and O^T += V^T P^T.  The TAIL
+  // Online softmax of tile t's scores `sacc`, with the scores of the next
+  // tile (K fragments kf, when DO_QK) computed in between: one MFMA of the
+  // next tile's chain per slice of this tile's exponentials, so that the
+  // matrix core and the vector ALU work at the same time.  The reference max
+  // is refreshed lazily, before the exponentials: only when some row's tile
+  // max exceeds it by more than 2^8 (a uniform branch, rarely taken after the
+  // first tiles) are the accumulators rescaled.  Produces the bf16 P
+  // fragments and this lane's share of the tile's row sum.  The TAIL
   // instantiation masks the keys past the end of the sequence (only the last
   // tile can need it).
-  auto softmax_pv = [&](auto tail_tag, const f32x16& sacc, int t, int slot) {
+  auto qk_softmax = [&](auto do_qk_tag, auto tail_tag, const f32x16& sacc, int t,
+                        const bf16x8 (&kf)[L::DS], bf16x8 (&pf)[2], float& tsum) {
+    constexpr bool DO_QK = decltype(do_qk_tag)::value;
     constexpr bool TAIL = decltype(tail_tag)::value;
-    const char* Vs = smem + slot * L::STAGE_B + L::TILE_B;
     // Accumulator register r holds key 8*(r/4) + 4*hh + r%4 of the tile.
     const int key0 = t * BN;
     auto valid = [&](int r) { return !TAIL || key0 + 8 * (r >> 2) + 4 * hh + (r & 3) < n_keys; };
@@ -307,10 +315,7 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
       const float v = valid(r) ? sacc[r] : (POS_SCALE ? -INFINITY : INFINITY);
       mraw = POS_SCALE ? fmaxf(mraw, v) : fminf(mraw, v);
     }
-    float mx = mraw * c;
-    mx = pair_max(mx);
-
-    // Lazy refresh of the reference max (uniform branch over the wave).
+    const float mx = pair_max(mraw * c);
     if (__any(mx > m_run + kLazyRescale)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -324,24 +329,36 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
 
     // P = exp2(S*c - m) rounded to bf16, straight into MFMA B fragments; the
     // row sum adds exactly the bf16 weights that enter P.V (packed dot with 1).
-    bf16x8 pf[2];
+    f32x16 snext = f32x16{};
     const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    constexpr int PER = 16 / L::DS;   // score registers per MFMA slice
+    tsum = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -m_run));
-      float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], c, -m_run));
-      if (!valid(r)) p0 = 0.0f;
-      if (!valid(r + 1)) p1 = 0.0f;
-      const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-      pf[r >> 3][r & 7] = pk[0];
-      pf[r >> 3][(r & 7) + 1] = pk[1];
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, one2, l_run, false);
+    for (int s = 0; s < L::DS; ++s) {
+      if (DO_QK) snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], snext, 0, 0, 0);
+#pragma unroll
+      for (int r = s * PER; r < (s + 1) * PER; r += 2) {
+        float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -m_run));
+        float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], c, -m_run));
+        if (!valid(r)) p0 = 0.0f;
+        if (!valid(r + 1)) p1 = 0.0f;
+        const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+        pf[r >> 3][r & 7] = pk[0];
+        pf[r >> 3][(r & 7) + 1] = pk[1];
+        tsum = __builtin_amdgcn_fdot2_f32_bf16(pk, one2, tsum, false);
+      }
     }
+    return snext;
+  };
 
-    // O^T += V^T P^T: two 16-key k-steps per 32-wide block of output columns.
-    // Element j of the V^T operand of k-step ks is key 16*ks + (j < 4 ? 4*hh + j
-    // : 8 + 4*hh + j - 4): the first transposing read covers j < 4, the second
-    // (8 rows further) j >= 4.
+  // Add the tile's row sum and O^T += V^T P^T for the tile in ring slot
+  // `slot`: two 16-key k-steps per 32-wide block of output columns.  Element
+  // j of the V^T operand of k-step ks is key 16*ks + (j < 4 ? 4*hh + j :
+  // 8 + 4*hh + j - 4): the first transposing read covers j < 4, the second
+  // (8 rows further) j >= 4.
+  auto finish_pv = [&](const bf16x8 (&pf)[2], float tsum, int slot) {
+    l_run += tsum;
+    const char* Vs = smem + slot * L::STAGE_B + L::TILE_B;
 #pragma unroll
     for (int db = 0; db < L::DB; ++db) {
 #pragma unroll
@@ -374,6 +391,24 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     barrier();
     if (i + NS - 2 < cnt) issue(t_begin + i + NS - 2, slot_of(i + NS - 2));
   };
+  // Tile i: softmax and P.V, with the scores of tile i+1 when DO_QK.
+  auto step = [&](auto do_qk_tag, auto tail_tag, int i, const f32x16& s_in) {
+    constexpr bool DO_QK = decltype(do_qk_tag)::value;
+    bf16x8 kf[L::DS];
+    if (DO_QK) {
+      const char* Ks = smem + slot_of(i + 1) * L::STAGE_B;
+#pragma unroll
+      for (int s = 0; s < L::DS; ++s)
+        kf[s] = *reinterpret_cast<const bf16x8*>(Ks + k_row_off + (((2 * s + hh) ^ fkl) << 4));
+    }
+    bf16x8 pf[2];
+    float tsum;
+    const f32x16 s_out = qk_softmax(do_qk_tag, tail_tag, s_in, t_begin + i, kf, pf, tsum);
+    finish_pv(pf, tsum, slot_of(i));
+    return s_out;
+  };
+  const std::true_type yes{};
+  const std::false_type no{};
 #pragma unroll
   for (int s = 0; s < NS - 2; ++s)
     if (s < cnt) issue(t_begin + s, s);
@@ -385,28 +420,33 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // Waves whose rows all lie past M run the same instruction stream on zero Q
   // rows (no branch in the loop) and store nothing.
   advance(0);
-  f32x16 s_cur = cnt > 0 ? qk(slot_of(0)) : f32x16{};
-  // Steady state: both groups have tiles i and i+1 (group 0 has at least
-  // nit - 1 tiles).
-  for (int i = 0; i + 2 < nit; ++i) {
+  f32x16 s_a = cnt > 0 ? qk(slot_of(0)) : f32x16{};
+  // Steady state, unrolled by two so that the score registers alternate
+  // instead of being copied: both groups have tiles i and i+1 (group 0 has at
+  // least nit - 1 tiles).
+  int i = 0;
+  for (; i + 3 < nit; i += 2) {
     advance(i + 1);
-    const f32x16 s_next = qk(slot_of(i + 1));
-    softmax_pv(std::false_type{}, s_cur, t_begin + i, slot_of(i));
-    s_cur = s_next;
+    const f32x16 s_b = step(yes, no, i, s_a);
+    advance(i + 2);
+    s_a = step(yes, no, i + 1, s_b);
   }
-  if (nit >= 2) {   // last iteration of the loop, peeled: group 0 may lack tile nit-1
+  if (i + 2 < nit) {
+    advance(i + 1);
+    s_a = step(yes, no, i, s_a);
+    ++i;
+  }
+  if (nit >= 2) {   // tile nit-2; group 0 may lack tile nit-1
     advance(nit - 1);
-    const f32x16 s_next = nit - 1 < cnt ? qk(slot_of(nit - 1)) : f32x16{};
-    softmax_pv(std::false_type{}, s_cur, t_begin + nit - 2, slot_of(nit - 2));
-    s_cur = s_next;
+    s_a = nit - 1 < cnt ? step(yes, no, nit - 2, s_a) : step(no, no, nit - 2, s_a);
   }
   // Only the last tile of the whole key sequence can run past its end; it is
   // always the group's tile nit-1.
   if (nit - 1 < cnt) {
     if (t_end * BN > n_keys)
-      softmax_pv(std::true_type{}, s_cur, t_begin + nit - 1, slot_of(nit - 1));
+      step(no, yes, nit - 1, s_a);
     else
-      softmax_pv(std::false_type{}, s_cur, t_begin + nit - 1, slot_of(nit - 1));
+      step(no, no, nit - 1, s_a);
   }
 
   float l_tot = l_run + __shfl_xor(l_run, 32);
