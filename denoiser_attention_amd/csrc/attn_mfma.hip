@@ -138,10 +138,19 @@ __device__ __forceinline__ void wait_tiles(int n_after) {
 // group 1 the trailing ceil(n/2)), each with its own LDS ring; their partial
 // softmax states are merged through LDS at the end.  KG = 2 supplies key-range
 // parallelism without writing split partials to memory.
-template <int D, int NS, int KG, bool OUT_BF16, bool POS_SCALE>
-__global__ __launch_bounds__(kThreads * KG, 2 / KG)
+//
+// RB = 1: each wave owns 32 query rows (128 per group), two waves per SIMD.
+// RB = 2 (KG = 1 only): each wave owns 64 rows as two 32-row blocks that
+// share every K and V fragment read from LDS (two MFMAs per fragment, two
+// independent score chains), halving the LDS traffic, the tile loads and the
+// barriers per unit of matrix work; one wave per SIMD, with the output
+// accumulators in the accumulation registers.
+template <int D, int NS, int KG, int RB, bool OUT_BF16, bool POS_SCALE>
+__global__ __launch_bounds__(kThreads * KG, RB == 2 ? 1 : 2 / KG)
 void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   using L = Lay<D>;
+  static_assert(RB == 1 || (RB == 2 && KG == 1), "64-row waves use one key group");
+  constexpr int WBM = 32 * RB * kWaves;   // packed query rows per group
   __shared__ __attribute__((aligned(1024))) char smem_all[KG * NS * L::STAGE_B];
 
   const int gtid = threadIdx.x;
@@ -187,20 +196,22 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
 
   // Packed row index of this (item, kv head)'s row 0 (split partials).
   const size_t prow_base = ((size_t)w * p.Hkv + kvh) * p.M;
-  const int wave_row0 = mt * BM + wave * 32;
-  const int r_local = wave_row0 + lr;
-  const bool row_ok = r_local < p.M;
+  const int wave_row0 = mt * WBM + wave * 32 * RB;
   const bool wave_active = wave_row0 < p.M;
 
-  // Q fragments: lane holds row r_local, columns 16s + 8hh .. +7 for every s.
-  bf16x8 qf[L::DS];
-  {
+  // Q fragments: for row block rb the lane holds row wave_row0 + 32*rb + lr,
+  // columns 16s + 8hh .. +7 for every s.
+  bf16x8 qf[RB][L::DS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r_local = wave_row0 + 32 * rb + lr;
+    const bool row_ok = r_local < p.M;
     const u32x4* src = reinterpret_cast<const u32x4*>(
         static_cast<const uint16_t*>(p.q) + (it.q_head0 + attn_row_off(p, row_ok ? r_local : 0)) * D);
 #pragma unroll
     for (int s = 0; s < L::DS; ++s) {
       const u32x4 v = row_ok ? src[2 * s + hh] : u32x4{0, 0, 0, 0};
-      qf[s] = __builtin_bit_cast(bf16x8, v);
+      qf[rb][s] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
@@ -272,24 +283,33 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     vofs[db] = key * L::ROWB + ((c ^ L::fv(gi >> 2)) << 4) + ((gi & 1) << 3);
   }
 
-  f32x16 oacc[L::DB];
+  f32x16 oacc[RB][L::DB];
 #pragma unroll
-  for (int db = 0; db < L::DB; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;   // reference max (base-2 scaled units)
-  float l_run = 0.0f;        // this lane's partial row sum (its 16 keys of each tile)
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int db = 0; db < L::DB; ++db) oacc[rb][db] = f32x16{};
+  float m_run[RB], l_run[RB];   // reference max (base-2 scaled units), this lane's row-sum share
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.0f;
+  }
   const float c = p.scale_log2;
+  typedef f32x16 Scores[RB];
 
   // S^T = K Q^T over the 32 keys of the tile in ring slot `slot`.
-  auto qk = [&](int slot) {
+  auto qk = [&](int slot, Scores& sacc) {
     const char* Ks = smem + slot * L::STAGE_B;
-    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) sacc[rb] = f32x16{};
 #pragma unroll
     for (int s = 0; s < L::DS; ++s) {
       const bf16x8 a =
           *reinterpret_cast<const bf16x8*>(Ks + k_row_off + (((2 * s + hh) ^ fkl) << 4));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc, 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        sacc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][s], sacc[rb], 0, 0, 0);
     }
-    return sacc;
   };
 
   // Online softmax of tile t's scores `sacc`, with the scores of the next
@@ -299,65 +319,87 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // is refreshed lazily, before the exponentials: only when some row's tile
   // max exceeds it by more than 2^8 (a uniform branch, rarely taken after the
   // first tiles) are the accumulators rescaled.  Produces the bf16 P
-  // fragments and this lane's share of the tile's row sum.  The TAIL
+  // fragments and this lane's share of the tile's row sums.  The TAIL
   // instantiation masks the keys past the end of the sequence (only the last
   // tile can need it).
-  auto qk_softmax = [&](auto do_qk_tag, auto tail_tag, const f32x16& sacc, int t,
-                        const bf16x8 (&kf)[L::DS], bf16x8 (&pf)[2], float& tsum) {
+  auto qk_softmax = [&](auto do_qk_tag, auto tail_tag, const Scores& sacc, int t,
+                        const bf16x8 (&kf)[L::DS], const char* Ks, bf16x8 (&pf)[RB][2],
+                        float (&tsum)[RB], Scores& snext) {
     constexpr bool DO_QK = decltype(do_qk_tag)::value;
     constexpr bool TAIL = decltype(tail_tag)::value;
     // Accumulator register r holds key 8*(r/4) + 4*hh + r%4 of the tile.
     const int key0 = t * BN;
     auto valid = [&](int r) { return !TAIL || key0 + 8 * (r >> 2) + 4 * hh + (r & 3) < n_keys; };
-    float mraw = POS_SCALE ? -INFINITY : INFINITY;
+    float mx[RB];
+    bool grow = false;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float v = valid(r) ? sacc[r] : (POS_SCALE ? -INFINITY : INFINITY);
-      mraw = POS_SCALE ? fmaxf(mraw, v) : fminf(mraw, v);
+    for (int rb = 0; rb < RB; ++rb) {
+      float mraw = POS_SCALE ? -INFINITY : INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float v = valid(r) ? sacc[rb][r] : (POS_SCALE ? -INFINITY : INFINITY);
+        mraw = POS_SCALE ? fmaxf(mraw, v) : fminf(mraw, v);
+      }
+      mx[rb] = pair_max(mraw * c);
+      grow = grow || mx[rb] > m_run[rb] + kLazyRescale;
     }
-    const float mx = pair_max(mraw * c);
-    if (__any(mx > m_run + kLazyRescale)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+    if (__any(grow)) {
 #pragma unroll
-      for (int db = 0; db < L::DB; ++db)
+      for (int rb = 0; rb < RB; ++rb) {
+        const float m_new = fmaxf(m_run[rb], mx[rb]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        l_run[rb] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m_run = m_new;
+        for (int db = 0; db < L::DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
+        m_run[rb] = m_new;
+      }
     }
 
     // P = exp2(S*c - m) rounded to bf16, straight into MFMA B fragments; the
     // row sum adds exactly the bf16 weights that enter P.V (packed dot with 1).
-    f32x16 snext = f32x16{};
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      snext[rb] = f32x16{};
+      tsum[rb] = 0.0f;
+    }
     const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
     constexpr int PER = 16 / L::DS;   // score registers per MFMA slice
-    tsum = 0.0f;
 #pragma unroll
     for (int s = 0; s < L::DS; ++s) {
-      if (DO_QK) snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], snext, 0, 0, 0);
+      // 32-row waves take the K fragments read up front; 64-row waves read
+      // each one just before its two MFMAs (fewer live registers).
+      bf16x8 ks_frag;
+      if (DO_QK)
+        ks_frag = RB == 1 ? kf[s]
+                          : *reinterpret_cast<const bf16x8*>(Ks + k_row_off + (((2 * s + hh) ^ fkl) << 4));
 #pragma unroll
-      for (int r = s * PER; r < (s + 1) * PER; r += 2) {
-        float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -m_run));
-        float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], c, -m_run));
-        if (!valid(r)) p0 = 0.0f;
-        if (!valid(r + 1)) p1 = 0.0f;
-        const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-        pf[r >> 3][r & 7] = pk[0];
-        pf[r >> 3][(r & 7) + 1] = pk[1];
-        tsum = __builtin_amdgcn_fdot2_f32_bf16(pk, one2, tsum, false);
+      for (int rb = 0; rb < RB; ++rb) {
+        if (DO_QK) snext[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ks_frag, qf[rb][s], snext[rb], 0, 0, 0);
+#pragma unroll
+        for (int r = s * PER; r < (s + 1) * PER; r += 2) {
+          float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][r], c, -m_run[rb]));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][r + 1], c, -m_run[rb]));
+          if (!valid(r)) p0 = 0.0f;
+          if (!valid(r + 1)) p1 = 0.0f;
+          const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+          pf[rb][r >> 3][r & 7] = pk[0];
+          pf[rb][r >> 3][(r & 7) + 1] = pk[1];
+          tsum[rb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one2, tsum[rb], false);
+        }
       }
     }
-    return snext;
   };
 
-  // Add the tile's row sum and O^T += V^T P^T for the tile in ring slot
-  // `slot`: two 16-key k-steps per 32-wide block of output columns.  Element
-  // j of the V^T operand of k-step ks is key 16*ks + (j < 4 ? 4*hh + j :
-  // 8 + 4*hh + j - 4): the first transposing read covers j < 4, the second
-  // (8 rows further) j >= 4.
-  auto finish_pv = [&](const bf16x8 (&pf)[2], float tsum, int slot) {
-    l_run += tsum;
+  // Add the tile's row sums and O^T += V^T P^T for the tile in ring slot
+  // `slot`: two 16-key k-steps per 32-wide block of output columns, each V^T
+  // fragment shared by the row blocks.  Element j of the V^T operand of k-step
+  // ks is key 16*ks + (j < 4 ? 4*hh + j : 8 + 4*hh + j - 4): the first
+  // transposing read covers j < 4, the second (8 rows further) j >= 4.
+  auto finish_pv = [&](const bf16x8 (&pf)[RB][2], const float (&tsum)[RB], int slot) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l_run[rb] += tsum[rb];
     const char* Vs = smem + slot * L::STAGE_B + L::TILE_B;
 #pragma unroll
     for (int db = 0; db < L::DB; ++db) {
@@ -366,9 +408,10 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
         const lds_char* vp = (const lds_char*)(Vs + vofs[db] + ks * 16 * L::ROWB);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * L::ROWB));
-        const i16x8 a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16),
-                                                            pf[ks], oacc[db], 0, 0, 0);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[rb][ks], oacc[rb][db], 0, 0, 0);
       }
     }
   };
@@ -392,20 +435,19 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     if (i + NS - 2 < cnt) issue(t_begin + i + NS - 2, slot_of(i + NS - 2));
   };
   // Tile i: softmax and P.V, with the scores of tile i+1 when DO_QK.
-  auto step = [&](auto do_qk_tag, auto tail_tag, int i, const f32x16& s_in) {
+  auto step = [&](auto do_qk_tag, auto tail_tag, int i, const Scores& s_in, Scores& s_out) {
     constexpr bool DO_QK = decltype(do_qk_tag)::value;
     bf16x8 kf[L::DS];
-    if (DO_QK) {
-      const char* Ks = smem + slot_of(i + 1) * L::STAGE_B;
+    const char* Ks = smem + slot_of(i + 1) * L::STAGE_B;
+    if (DO_QK && RB == 1) {
 #pragma unroll
       for (int s = 0; s < L::DS; ++s)
         kf[s] = *reinterpret_cast<const bf16x8*>(Ks + k_row_off + (((2 * s + hh) ^ fkl) << 4));
     }
-    bf16x8 pf[2];
-    float tsum;
-    const f32x16 s_out = qk_softmax(do_qk_tag, tail_tag, s_in, t_begin + i, kf, pf, tsum);
+    bf16x8 pf[RB][2];
+    float tsum[RB];
+    qk_softmax(do_qk_tag, tail_tag, s_in, t_begin + i, kf, Ks, pf, tsum, s_out);
     finish_pv(pf, tsum, slot_of(i));
-    return s_out;
   };
   const std::true_type yes{};
   const std::false_type no{};
@@ -416,45 +458,62 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // Consuming Q here makes its (conservative, full) load wait overlap the K/V
   // latency and keeps it out of the pipelined loop.
 #pragma unroll
-  for (int s = 0; s < L::DS; ++s) consume(qf[s]);
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int s = 0; s < L::DS; ++s) consume(qf[rb][s]);
   // Waves whose rows all lie past M run the same instruction stream on zero Q
   // rows (no branch in the loop) and store nothing.
   advance(0);
-  f32x16 s_a = cnt > 0 ? qk(slot_of(0)) : f32x16{};
+  Scores s_a, s_b;
+  if (cnt > 0) {
+    qk(slot_of(0), s_a);
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) s_a[rb] = f32x16{};
+  }
   // Steady state, unrolled by two so that the score registers alternate
   // instead of being copied: both groups have tiles i and i+1 (group 0 has at
   // least nit - 1 tiles).
   int i = 0;
   for (; i + 3 < nit; i += 2) {
     advance(i + 1);
-    const f32x16 s_b = step(yes, no, i, s_a);
+    step(yes, no, i, s_a, s_b);
     advance(i + 2);
-    s_a = step(yes, no, i + 1, s_b);
+    step(yes, no, i + 1, s_b, s_a);
   }
   if (i + 2 < nit) {
     advance(i + 1);
-    s_a = step(yes, no, i, s_a);
+    step(yes, no, i, s_a, s_b);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) s_a[rb] = s_b[rb];
     ++i;
   }
   if (nit >= 2) {   // tile nit-2; group 0 may lack tile nit-1
     advance(nit - 1);
-    s_a = nit - 1 < cnt ? step(yes, no, nit - 2, s_a) : step(no, no, nit - 2, s_a);
+    if (nit - 1 < cnt)
+      step(yes, no, nit - 2, s_a, s_b);
+    else
+      step(no, no, nit - 2, s_a, s_b);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) s_a[rb] = s_b[rb];
   }
   // Only the last tile of the whole key sequence can run past its end; it is
   // always the group's tile nit-1.
   if (nit - 1 < cnt) {
     if (t_end * BN > n_keys)
-      step(no, yes, nit - 1, s_a);
+      step(no, yes, nit - 1, s_a, s_b);
     else
-      step(no, no, nit - 1, s_a);
+      step(no, no, nit - 1, s_a, s_b);
   }
 
-  float l_tot = l_run + __shfl_xor(l_run, 32);
-  // Staging tile for the output: each wave writes its normalised 32 x D block
-  // to LDS (fp32, 16-byte chunk c of row r at chunk position c ^ (r & 7), so
-  // that both the accumulator-order writes and the row-order reads spread over
-  // all banks) and reads it back row by row, so that the global stores cover
-  // whole contiguous rows.
+  float l_tot[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) l_tot[rb] = l_run[rb] + __shfl_xor(l_run[rb], 32);
+  // Staging tile for the output: each wave writes a normalised 32 x D row
+  // block to LDS (fp32, 16-byte chunk c of row r at chunk position c ^ (r & 7),
+  // so that both the accumulator-order writes and the row-order reads spread
+  // over all banks) and reads it back row by row, so that the global stores
+  // cover whole contiguous rows.
   float* stg;
   if (KG == 2) {
     // Merge group 1's (max, sum, O) into group 0 through LDS (the rings are
@@ -466,25 +525,25 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
 #pragma unroll
       for (int db = 0; db < L::DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xbuf[(db * 16 + r) * 64 + lane] = oacc[db][r];
-      xbuf[(L::DB * 16) * 64 + lane] = m_run;
-      xbuf[(L::DB * 16 + 1) * 64 + lane] = l_tot;
+        for (int r = 0; r < 16; ++r) xbuf[(db * 16 + r) * 64 + lane] = oacc[0][db][r];
+      xbuf[(L::DB * 16) * 64 + lane] = m_run[0];
+      xbuf[(L::DB * 16 + 1) * 64 + lane] = l_tot[0];
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     barrier();
     if (kgrp == 1) return;
     const float m1 = xbuf[(L::DB * 16) * 64 + lane];
     const float l1 = xbuf[(L::DB * 16 + 1) * 64 + lane];
-    const float m_new = fmaxf(m_run, m1);
-    const float a0 = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 for an empty group
+    const float m_new = fmaxf(m_run[0], m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run[0] - m_new);   // 0 for an empty group
     const float a1 = __builtin_amdgcn_exp2f(m1 - m_new);
 #pragma unroll
     for (int db = 0; db < L::DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        oacc[db][r] = oacc[db][r] * a0 + xbuf[(db * 16 + r) * 64 + lane] * a1;
-    l_tot = l_tot * a0 + l1 * a1;
-    m_run = m_new;
+        oacc[0][db][r] = oacc[0][db][r] * a0 + xbuf[(db * 16 + r) * 64 + lane] * a1;
+    l_tot[0] = l_tot[0] * a0 + l1 * a1;
+    m_run[0] = m_new;
     // This wave alone reads and then rewrites its own exchange area (LDS
     // operations of one wave complete in order).
     stg = xbuf;
@@ -495,55 +554,63 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   static_assert(32 * D <= (L::DB * 16 + 2) * 64, "staging tile fits the exchange area");
   static_assert(kWaves * 32 * D * 4 <= NS * L::STAGE_B, "staging tiles fit the ring");
   if (!wave_active) return;
-  const float inv = 1.0f / l_tot;
+  const size_t rows_total = (size_t)p.B * p.NB * p.Hq * p.L;
 #pragma unroll
-  for (int db = 0; db < L::DB; ++db)
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row0 = wave_row0 + 32 * rb;           // first packed row of this block
+    const int rows_here = min(32, p.M - row0);      // valid rows of this block
+    if (rows_here <= 0) break;
+    const float inv = 1.0f / l_tot[rb];
+    // The previous block's row reads are complete before these writes: the
+    // same wave's LDS operations complete in order.
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int chunk = db * 8 + 2 * g + hh;
-      *reinterpret_cast<f32x4*>(stg + lr * D + ((chunk ^ (lr & 7)) << 2)) =
-          f32x4{oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
-                oacc[db][4 * g + 3] * inv};
-    }
-  asm volatile("" ::: "memory");
-  const int rows_here = min(32, p.M - wave_row0);   // valid rows of this wave
-  if (OUT_BF16) {
-    // 8 values (16 bytes) per lane, D/8 lanes per row.
-    constexpr int LPR = D / 8, RPI = 64 / LPR;
+    for (int db = 0; db < L::DB; ++db)
 #pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int row = i * RPI + lane / LPR, c8 = lane % LPR;
-      const f32x4 a = *reinterpret_cast<const f32x4*>(stg + row * D + (((2 * c8) ^ (row & 7)) << 2));
-      const f32x4 bq = *reinterpret_cast<const f32x4*>(stg + row * D + (((2 * c8 + 1) ^ (row & 7)) << 2));
-      u32x4 pk;
-      pk.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a.x) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a.y) << 16);
-      pk.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a.z) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a.w) << 16);
-      pk.z = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.x) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.y) << 16);
-      pk.w = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.z) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.w) << 16);
-      if (row < rows_here) {
-        const size_t orow = it.q_head0 + attn_row_off(p, wave_row0 + row);
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + orow * D + 8 * c8) = pk;
+      for (int g = 0; g < 4; ++g) {
+        const int chunk = db * 8 + 2 * g + hh;
+        *reinterpret_cast<f32x4*>(stg + lr * D + ((chunk ^ (lr & 7)) << 2)) =
+            f32x4{oacc[rb][db][4 * g] * inv, oacc[rb][db][4 * g + 1] * inv,
+                  oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv};
       }
-    }
-  } else {
-    // 4 values (16 bytes) per lane, D/4 lanes per row: the final fp32 output,
-    // or this split's partial.
-    constexpr int LPR = D / 4, RPI = 64 / LPR;
-    const size_t rows_total = (size_t)p.B * p.NB * p.Hq * p.L;
-    float* part = p.part_o + ((size_t)split * rows_total + prow_base + wave_row0) * D;
+    asm volatile("" ::: "memory");
+    if (OUT_BF16) {
+      // 8 values (16 bytes) per lane, D/8 lanes per row.
+      constexpr int LPR = D / 8, RPI = 64 / LPR;
 #pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int row = i * RPI + lane / LPR, c4 = lane % LPR;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(stg + row * D + ((c4 ^ (row & 7)) << 2));
-      if (row < rows_here) {
-        float* dst = p.splits == 1
-                         ? static_cast<float*>(p.out) + (it.q_head0 + attn_row_off(p, wave_row0 + row)) * D
-                         : part + (size_t)row * D;
-        *reinterpret_cast<f32x4*>(dst + 4 * c4) = v;
+      for (int i2 = 0; i2 < 32 / RPI; ++i2) {
+        const int row = i2 * RPI + lane / LPR, c8 = lane % LPR;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(stg + row * D + (((2 * c8) ^ (row & 7)) << 2));
+        const f32x4 bq = *reinterpret_cast<const f32x4*>(stg + row * D + (((2 * c8 + 1) ^ (row & 7)) << 2));
+        u32x4 pk;
+        pk.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a.x) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a.y) << 16);
+        pk.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a.z) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a.w) << 16);
+        pk.z = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.x) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.y) << 16);
+        pk.w = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.z) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)bq.w) << 16);
+        if (row < rows_here) {
+          const size_t orow = it.q_head0 + attn_row_off(p, row0 + row);
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + orow * D + 8 * c8) = pk;
+        }
       }
+    } else {
+      // 4 values (16 bytes) per lane, D/4 lanes per row: the final fp32 output,
+      // or this split's partial.
+      constexpr int LPR = D / 4, RPI = 64 / LPR;
+      float* part = p.part_o + ((size_t)split * rows_total + prow_base + row0) * D;
+#pragma unroll
+      for (int i2 = 0; i2 < 32 / RPI; ++i2) {
+        const int row = i2 * RPI + lane / LPR, c4 = lane % LPR;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stg + row * D + ((c4 ^ (row & 7)) << 2));
+        if (row < rows_here) {
+          float* dst = p.splits == 1
+                           ? static_cast<float*>(p.out) + (it.q_head0 + attn_row_off(p, row0 + row)) * D
+                           : part + (size_t)row * D;
+          *reinterpret_cast<f32x4*>(dst + 4 * c4) = v;
+        }
+      }
+      if (p.splits > 1 && hh == 0 && lr < rows_here)
+        p.part_lse[(size_t)split * rows_total + prow_base + row0 + lr] = m_run[rb] + __log2f(l_tot[rb]);
     }
-    if (p.splits > 1 && hh == 0 && row_ok)
-      p.part_lse[(size_t)split * rows_total + prow_base + r_local] = m_run + __log2f(l_tot);
+    asm volatile("" ::: "memory");
   }
 }
 
@@ -551,15 +618,25 @@ constexpr int kStages = 4;
 
 template <int D, bool OUT_BF16, bool POS>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
-  const int m_tiles = (p.M + BM - 1) / BM;
+  const int rows_wg = p.rows_per_wave == 64 ? 2 * BM : BM;
+  const int m_tiles = (p.M + rows_wg - 1) / rows_wg;
   const long long n = (long long)m_tiles * p.splits * p.B * p.NB * p.Hkv;
   if (n <= 0 || n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (p.kgroups == 2)
-    hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 2, OUT_BF16, POS>), dim3((unsigned)n),
+  if (p.rows_per_wave == 64) {
+    if constexpr (D == 128) {
+      if (p.kgroups != 1) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, 2, OUT_BF16, POS>), dim3((unsigned)n),
+                         dim3(kThreads), 0, stream, p, m_tiles, (int)n);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (p.kgroups == 2) {
+    hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 2, 1, OUT_BF16, POS>), dim3((unsigned)n),
                        dim3(2 * kThreads), 0, stream, p, m_tiles, (int)n);
-  else
-    hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, OUT_BF16, POS>), dim3((unsigned)n),
+  } else {
+    hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, 1, OUT_BF16, POS>), dim3((unsigned)n),
                        dim3(kThreads), 0, stream, p, m_tiles, (int)n);
+  }
   return hipGetLastError();
 }
 

@@ -40,6 +40,7 @@ tt_status device_present() {
 struct AttnPlan {
   int path = TT_ATTN_SHUFFLE;  // resolved family
   int kgroups = 1;             // MFMA: wave groups splitting a workgroup's keys
+  int rows_per_wave = 32;      // MFMA: query rows per wavefront
   int splits = 1;
   int tiles_per_split = 1;
   bool empty = false;          // nothing to compute
@@ -62,6 +63,8 @@ tt_status plan_attn(long long B, int P, int L, int Hq, int Hkv, int D, tt_dtype 
   if (req != TT_ATTN_AUTO && req != TT_ATTN_MFMA && req != TT_ATTN_SHUFFLE) return TT_EINVAL;
   if (opts && opts->kv_splits < 0) return TT_EINVAL;
   if (opts && (opts->kv_groups < 0 || opts->kv_groups > 2)) return TT_EINVAL;
+  if (opts && opts->rows_per_wave != 0 && opts->rows_per_wave != 32 && opts->rows_per_wave != 64)
+    return TT_EINVAL;
   if ((long long)P + L > INT_MAX / 2) return TT_EUNSUPPORTED;
   const int G = Hq / Hkv;
   const long long M = (long long)G * L;
@@ -98,13 +101,21 @@ tt_status plan_attn(long long B, int P, int L, int Hq, int Hkv, int D, tt_dtype 
     // workgroup split each workgroup's key range on chip, and workgroups split
     // it further (with a merge pass) only as far as still needed.
     n_tiles = cdiv(n_keys, tt::kAttnMfmaBN);
-    const long long base = cdiv(M, tt::kAttnMfmaBM) * B * Hkv;
     const int req_groups = opts ? opts->kv_groups : 0;
-    plan->kgroups = req_groups ? req_groups : (base >= kMfmaTargetWG ? 1 : 2);
+    const int req_rows = opts ? opts->rows_per_wave : 0;
+    // 64-row waves only on request: with one wave per SIMD they have measured
+    // slower than 32-row waves at two waves per SIMD on every workload here.
+    const long long base64 = cdiv(M, 2 * tt::kAttnMfmaBM) * B * Hkv;
+    const bool rows64 = req_rows == 64;
+    if (rows64 && (D != 128 || req_groups == 2)) return TT_EUNSUPPORTED;
+    plan->rows_per_wave = rows64 ? 64 : 32;
+    const long long base = rows64 ? base64 : cdiv(M, tt::kAttnMfmaBM) * B * Hkv;
+    const long long target = rows64 ? kMfmaTargetWG / 2 : kMfmaTargetWG;
+    plan->kgroups = rows64 ? 1 : (req_groups ? req_groups : (base >= kMfmaTargetWG ? 1 : 2));
     if (opts && opts->kv_splits > 0) {
       splits = opts->kv_splits < n_tiles ? opts->kv_splits : n_tiles;
     } else {
-      splits = cdiv(kMfmaTargetWG / plan->kgroups, base);
+      splits = cdiv(target / plan->kgroups, base);
       const long long min_tiles = 2 * plan->kgroups;   // per workgroup
       const long long max_splits = n_tiles / min_tiles > 1 ? n_tiles / min_tiles : 1;
       if (splits > max_splits) splits = max_splits;
@@ -252,6 +263,7 @@ tt_status attn_run(const AttnCall& c) {
   p.splits = plan.splits;
   p.tiles_per_split = plan.tiles_per_split;
   p.kgroups = plan.kgroups;
+  p.rows_per_wave = plan.rows_per_wave;
   p.out_bf16 = c.out_dtype == TT_BF16 ? 1 : 0;
   p.scale_log2 = c.scale * kLog2e;
   if (plan.splits > 1) {

@@ -42,6 +42,7 @@ struct AttnParams {
   int splits;          // key-range splits per query tile (>= 1), one workgroup each
   int tiles_per_split; // key tiles handled by one split
   int kgroups;         // MFMA kernel: 1 or 2 key groups inside a workgroup
+  int rows_per_wave;   // MFMA kernel: 32, or 64 (head_dim 128, one key group)
   int out_bf16;        // 1: write bf16 output, 0: fp32
   float scale_log2;    // softmax scale * log2(e)
 };

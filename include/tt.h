@@ -64,11 +64,15 @@ typedef enum { TT_ATTN_AUTO = 0, TT_ATTN_MFMA = 1, TT_ATTN_SHUFFLE = 2 } tt_attn
  * forces that many (clamped so that no split is empty; partial results are then
  * merged in a second pass).  kv_groups (MFMA kernel only) = 0 lets the library
  * choose, 1 or 2 forces how many wave groups inside one workgroup divide that
- * workgroup's key range between them (merged on chip). */
+ * workgroup's key range between them (merged on chip).  rows_per_wave (MFMA
+ * kernel only) = 0 lets the library choose, 32 or 64 forces how many query rows
+ * one wavefront owns; 64 needs head_dim 128 and one wave group (otherwise
+ * TT_EUNSUPPORTED). */
 typedef struct {
-  int path;       /* tt_attn_path */
-  int kv_splits;  /* 0 = auto */
-  int kv_groups;  /* 0 = auto, 1 or 2 */
+  int path;           /* tt_attn_path */
+  int kv_splits;      /* 0 = auto */
+  int kv_groups;      /* 0 = auto, 1 or 2 */
+  int rows_per_wave;  /* 0 = auto, 32 or 64 */
 } tt_attn_opts;
 
 /* Human-readable name of a status code (static storage, never NULL). */

@@ -63,6 +63,7 @@ def attn_call(**kw):
     dict(hq=6, hkv=4), dict(pcap=10), dict(scale=float("inf")), dict(scale=float("nan")),
     dict(dtype=7), dict(odt=7), dict(dtype=B.TT_FP32, odt=B.TT_BF16),
     dict(opts=(9, 0, 0)), dict(opts=(0, -1, 0)), dict(opts=(0, 0, 3)), dict(opts=(0, 0, -1)),
+    dict(opts=(0, 0, 0, 48)), dict(opts=(0, 0, 0, -32)),
     # bf16 with a split that needs a workspace, none given
     dict(dtype=B.TT_BF16, odt=B.TT_BF16, hq=32, hkv=2, d=128, prefix_len=2048, pcap=2048,
          block_len=32, batch=8, opts=(B.TT_ATTN_MFMA, 4, 0)),
@@ -74,6 +75,9 @@ def test_attn_rejects_invalid(kw):
 @pytest.mark.parametrize("kw", [
     dict(d=96), dict(d=32), dict(opts=(B.TT_ATTN_MFMA, 0, 0)),         # fp32 on MFMA
     dict(dtype=B.TT_BF16, odt=B.TT_BF16, d=256, opts=(B.TT_ATTN_MFMA, 0, 0)),
+    # 64-row waves: head_dim 128 and one wave group only
+    dict(dtype=B.TT_BF16, odt=B.TT_BF16, d=64, opts=(B.TT_ATTN_MFMA, 0, 0, 64)),
+    dict(dtype=B.TT_BF16, odt=B.TT_BF16, d=128, opts=(B.TT_ATTN_MFMA, 0, 2, 64)),
 ])
 def test_attn_unsupported(kw):
     assert attn_call(**kw) == B.TT_EUNSUPPORTED

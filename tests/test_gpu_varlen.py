@@ -81,6 +81,14 @@ def test_varlen_splits_and_groups(groups, splits):
     check_attn(got, oracle_varlen(inp), "bf16", False, f"varlen groups={groups} splits={splits}")
 
 
+@pytest.mark.parametrize("splits", [0, 2])
+def test_varlen_rows64(splits):
+    cfg = base_cfg(batch=5, block_len=40)
+    inp = synth.varlen_inputs(cfg, seed=16, max_prefix_len=400, prefix_cap=410)
+    got = gpu_varlen(inp, path="mfma", rows_per_wave=64, kv_splits=splits, out_dtype=torch.float32)
+    check_attn(got, oracle_varlen(inp), "bf16", False, f"varlen rows64 splits={splits}")
+
+
 def test_varlen_fp32():
     cfg = synth.get_config("tiny_fp32")
     inp = synth.varlen_inputs(cfg, seed=13, batch=4, max_prefix_len=53, prefix_cap=70)
@@ -170,6 +178,14 @@ def test_multiblock_splits_and_groups(groups, splits):
                          out_dtype=torch.float32)
     check_attn(got, oracle_multiblock(inp), "bf16", False,
                f"multiblock groups={groups} splits={splits}")
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_multiblock_rows64(splits):
+    cfg = base_cfg(batch=2, n_q_heads=16, n_kv_heads=2)
+    inp = synth.multiblock_inputs(cfg, 5, 40, seed=25)
+    got = gpu_multiblock(inp, path="mfma", rows_per_wave=64, kv_splits=splits)
+    check_attn(got, oracle_multiblock(inp), "bf16", True, f"multiblock rows64 splits={splits}")
 
 
 def test_multiblock_fp32():
