@@ -15,12 +15,13 @@
 //   shuffles and across the 4 waves through LDS, ties going to the lower id at
 //   every stage.  Chunks of unmasked rows exit at once.
 // topk_commit_kernel -- one workgroup per sequence: merges the chunk triples of
-//   each masked position in chunk order, forms the confidence, ranks every
-//   masked position by counting the masked positions ahead of it in the order
-//   (confidence descending, position ascending; position ascending alone for
-//   the mock-autoregressive rule), 16 confidences per step, and commits
-//   rank < k, where k comes from the selection rule: fixed, or derived from
-//   the sequence's masked count and its count of confidences above gamma.
+//   each masked position (one thread per position, in chunk order), forms the
+//   confidence, ranks every masked position by counting the positions ahead
+//   of it in the order (confidence descending, position ascending) with one
+//   64-bit key comparison each (or by counting the masked positions before it,
+//   for the mock-autoregressive rule), and commits rank < k, where k comes
+//   from the selection rule: fixed, or derived from the sequence's masked
+//   count and its count of confidences above gamma.
 #include <climits>
 
 #include "tt_internal.h"
@@ -34,7 +35,6 @@ constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kVecPerThread = kVocabChunk / (kThreads * 4);      // 8 float4 loads
 constexpr int kScalarPerThread = kVocabChunk / kThreads;         // 32 scalar loads
-constexpr int kMergeBatch = 16;                                  // partial loads in flight per position
 static_assert(kVocabChunk % (kThreads * 4) == 0, "chunk must be a multiple of 1024");
 
 struct Triple {
@@ -145,32 +145,36 @@ __global__ __launch_bounds__(kThreads) void vocab_reduce_kernel(UnmaskParams p) 
 }
 
 __global__ __launch_bounds__(kThreads) void topk_commit_kernel(UnmaskParams p) {
-  // Confidences of the sequence; positions that are not masked hold -2, which
-  // never compares >= a real confidence (those lie in (0, 1]).  The array is
-  // padded with -2 to a multiple of 16 for the rank loop.
-  __shared__ __attribute__((aligned(16))) float s_conf[kUnmaskMaxL];
+  // Ranking key of each position: (bits of conf) << 32 | (2^32 - 1 - position)
+  // for a masked position, 0 otherwise.  conf is positive, so its bits order
+  // like its value, and one unsigned 64-bit comparison orders the positions
+  // by (conf descending, position ascending); unmasked positions (and the
+  // padding to a multiple of 16) never rank ahead of a masked one.
+  __shared__ __attribute__((aligned(16))) uint64_t s_key[kUnmaskMaxL];
   __shared__ int s_pred[kUnmaskMaxL];
+  __shared__ uint64_t s_bits[kUnmaskMaxL / 64];   // masked flags, 64 positions per word
+  __shared__ int s_count[2];   // masked positions, masked positions with conf > gamma
 
   const int b = blockIdx.x;
   const int L = p.L;
   const int L16 = (L + 15) >> 4;
   const int tid = threadIdx.x;
   const size_t row0 = (size_t)b * L;
-
-  __shared__ int s_count[2];   // masked positions, masked positions with conf > gamma
   if (tid < 2) s_count[tid] = 0;
-  __syncthreads();
-  int my_masked = 0, my_above = 0;
+  for (int l = L + tid; l < 16 * L16; l += kThreads) s_key[l] = 0;
 
-  // Every mask flag of the sequence is read before any is written, so
-  // mask_out may alias mask_state.
-  for (int l = tid; l < 16 * L16; l += kThreads) {
-    float conf = -2.0f;
+  // Merge: one thread per position combines the position's chunk triples in
+  // chunk order from a batch of independent 16-byte loads.  Every mask flag of
+  // the sequence is read before any is written, so mask_out may alias
+  // mask_state.
+  constexpr int kMergeBatch = 16;
+  int my_masked = 0, my_above = 0;
+  for (int l = tid; l < L; l += kThreads) {
+    uint64_t key = 0;
     int pred = -1;
-    if (l < L && p.mask_state[row0 + l] != 0) {
+    if (p.mask_state[row0 + l] != 0) {
       const VocabPartial* pp = p.partials + (row0 + l) * (size_t)p.n_chunks;
       Triple t{-INFINITY, INT_MAX, 0.0f};
-      // Issue a batch of independent 16-byte loads, then merge in chunk order.
       for (int c0 = 0; c0 < p.n_chunks; c0 += kMergeBatch) {
         VocabPartial q[kMergeBatch];
 #pragma unroll
@@ -180,17 +184,29 @@ __global__ __launch_bounds__(kThreads) void topk_commit_kernel(UnmaskParams p) {
         for (int i = 0; i < kMergeBatch; ++i)
           if (c0 + i < p.n_chunks) t = combine(t, Triple{q[i].m, q[i].arg, q[i].s});
       }
-      conf = 1.0f / t.s;
+      const float conf = 1.0f / t.s;
+      key = ((uint64_t)__float_as_uint(conf) << 32) | (uint64_t)(0xffffffffu - (uint32_t)l);
       pred = t.arg;
       ++my_masked;
       my_above += conf > p.gamma ? 1 : 0;
     }
-    s_conf[l] = conf;
-    if (l < L) s_pred[l] = pred;
+    s_key[l] = key;
+    s_pred[l] = pred;
   }
+  __syncthreads();
   if (p.mode == kSelThreshold || p.mode == kSelSchedule) {
     if (my_masked) atomicAdd(&s_count[0], my_masked);
     if (my_above) atomicAdd(&s_count[1], my_above);
+  }
+  const bool leftmost = p.mode == kSelLeftmost;
+  if (leftmost) {
+    // Masked flags as bit words (each wave covers 64 positions at a time).
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int w = wave; w < (L + 63) / 64; w += kThreads / 64) {
+      const int l = 64 * w + lane;
+      const unsigned long long bal = __ballot(l < L && s_key[l] != 0);
+      if (lane == 0) s_bits[w] = bal;
+    }
   }
   __syncthreads();
 
@@ -203,35 +219,32 @@ __global__ __launch_bounds__(kThreads) void topk_commit_kernel(UnmaskParams p) {
     const long long keep = (long long)L * (p.n_steps - p.step) / p.n_steps;
     k = (int)max(0LL, (long long)s_count[0] - keep);
   }
-  const bool leftmost = p.mode == kSelLeftmost;
 
-  // rank(l) = #{masked j : conf_j > conf_l, or conf_j == conf_l and j < l};
-  // commit when rank < k.  Every lane reads the same LDS words (broadcast),
-  // 16 confidences per iteration from four independent 16-byte reads.
-  const f32x4* c4 = reinterpret_cast<const f32x4*>(s_conf);
+  // rank(l) = #{j : key_j > key_l} (or, mock-autoregressive, the masked
+  // positions before l); commit when rank < k.  Every lane reads the same LDS
+  // words (broadcast), 16 keys per iteration.
+  typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+  const u64x2* k2 = reinterpret_cast<const u64x2*>(s_key);
   for (int l = tid; l < L; l += kThreads) {
     const size_t row = row0 + l;
-    const float c = s_conf[l];
-    const bool masked = c > -1.0f;
+    const uint64_t kl = s_key[l];
+    const bool masked = kl != 0;
     int ahead = 0;
     if (masked && k > 0 && leftmost) {
-      // Masked positions before l.
-      for (int j = 0; j < l; ++j) ahead += s_conf[j] > -1.0f ? 1 : 0;
+      const int w = l >> 6;
+      for (int i = 0; i < w; ++i) ahead += __popcll(s_bits[i]);
+      ahead += __popcll(s_bits[w] & ((1ull << (l & 63)) - 1ull));
     } else if (masked && k > 0) {
       for (int j16 = 0; j16 < L16; ++j16) {
-        f32x4 v[4];
+        u64x2 v[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = c4[4 * j16 + u];
+        for (int u = 0; u < 8; ++u) v[u] = k2[8 * j16 + u];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = 16 * j16 + 4 * u + e;
-            ahead += (v[u][e] > c || (v[u][e] == c && j < l)) ? 1 : 0;
-          }
+        for (int u = 0; u < 8; ++u) ahead += (v[u].x > kl ? 1 : 0) + (v[u].y > kl ? 1 : 0);
       }
     }
     const bool commit = masked && ahead < k;
+    const float c = __uint_as_float((uint32_t)(kl >> 32));
     if (commit) p.tokens_out[row] = s_pred[l];
     p.mask_out[row] = (masked && !commit) ? 1 : 0;
     if (p.conf_out) p.conf_out[row] = masked ? c : -1.0f;
