@@ -434,11 +434,17 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     barrier();
     if (i + NS - 2 < cnt) issue(t_begin + i + NS - 2, slot_of(i + NS - 2));
   };
-  // Tile i: softmax and P.V, with the scores of tile i+1 when DO_QK.
-  auto step = [&](auto do_qk_tag, auto tail_tag, int i, const Scores& s_in, Scores& s_out) {
+  // Tile i (in ring slot `slot`): softmax and P.V, with the scores of tile
+  // i+1 when DO_QK.  `slot` is an int or, in the loop unrolled by the ring
+  // depth, a compile-time constant, so that the slot offsets fold into the
+  // LDS reads' immediate offsets.
+  auto step = [&](auto do_qk_tag, auto tail_tag, int i, const Scores& s_in, Scores& s_out,
+                  auto slot) {
     constexpr bool DO_QK = decltype(do_qk_tag)::value;
+    const int v_slot = slot;
+    const int k_slot = (v_slot + 1) & (NS - 1);
     bf16x8 kf[L::DS];
-    const char* Ks = smem + slot_of(i + 1) * L::STAGE_B;
+    const char* Ks = smem + k_slot * L::STAGE_B;
     if (DO_QK && RB == 1) {
 #pragma unroll
       for (int s = 0; s < L::DS; ++s)
@@ -447,7 +453,7 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     bf16x8 pf[RB][2];
     float tsum[RB];
     qk_softmax(do_qk_tag, tail_tag, s_in, t_begin + i, kf, Ks, pf, tsum, s_out);
-    finish_pv(pf, tsum, slot_of(i));
+    finish_pv(pf, tsum, v_slot);
   };
   const std::true_type yes{};
   const std::false_type no{};
@@ -475,15 +481,29 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // instead of being copied: both groups have tiles i and i+1 (group 0 has at
   // least nit - 1 tiles).
   int i = 0;
+  if constexpr (NS == 4) {
+    // Unrolled by the ring depth: i stays a multiple of 4, so tile i + j
+    // lives in slot j.
+    for (; i + 5 < nit; i += 4) {
+      advance(i + 1);
+      step(yes, no, i, s_a, s_b, std::integral_constant<int, 0>{});
+      advance(i + 2);
+      step(yes, no, i + 1, s_b, s_a, std::integral_constant<int, 1>{});
+      advance(i + 3);
+      step(yes, no, i + 2, s_a, s_b, std::integral_constant<int, 2>{});
+      advance(i + 4);
+      step(yes, no, i + 3, s_b, s_a, std::integral_constant<int, 3>{});
+    }
+  }
   for (; i + 3 < nit; i += 2) {
     advance(i + 1);
-    step(yes, no, i, s_a, s_b);
+    step(yes, no, i, s_a, s_b, slot_of(i));
     advance(i + 2);
-    step(yes, no, i + 1, s_b, s_a);
+    step(yes, no, i + 1, s_b, s_a, slot_of(i + 1));
   }
   if (i + 2 < nit) {
     advance(i + 1);
-    step(yes, no, i, s_a, s_b);
+    step(yes, no, i, s_a, s_b, slot_of(i));
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) s_a[rb] = s_b[rb];
     ++i;
@@ -491,9 +511,9 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   if (nit >= 2) {   // tile nit-2; group 0 may lack tile nit-1
     advance(nit - 1);
     if (nit - 1 < cnt)
-      step(yes, no, nit - 2, s_a, s_b);
+      step(yes, no, nit - 2, s_a, s_b, slot_of(nit - 2));
     else
-      step(no, no, nit - 2, s_a, s_b);
+      step(no, no, nit - 2, s_a, s_b, slot_of(nit - 2));
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) s_a[rb] = s_b[rb];
   }
@@ -501,9 +521,9 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // always the group's tile nit-1.
   if (nit - 1 < cnt) {
     if (t_end * BN > n_keys)
-      step(no, yes, nit - 1, s_a, s_b);
+      step(no, yes, nit - 1, s_a, s_b, slot_of(nit - 1));
     else
-      step(no, no, nit - 1, s_a, s_b);
+      step(no, no, nit - 1, s_a, s_b, slot_of(nit - 1));
   }
 
   float l_tot[RB];
