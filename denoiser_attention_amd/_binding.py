@@ -32,7 +32,7 @@ class TTError(RuntimeError):
 
 class AttnOpts(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("kv_splits", ctypes.c_int), ("kv_groups", ctypes.c_int),
-                ("rows_per_wave", ctypes.c_int)]
+                ("rows_per_wave", ctypes.c_int), ("stream_waves", ctypes.c_int)]
 
 
 class Select(ctypes.Structure):
@@ -146,8 +146,8 @@ def _cuda_contig(name: str, t: torch.Tensor, device: torch.device) -> None:
 
 def attn_workspace_bytes(batch, prefix_len, block_len, n_q_heads, n_kv_heads, head_dim,
                          dtype: torch.dtype, path: str = "auto", kv_splits: int = 0,
-                         kv_groups: int = 0, rows_per_wave: int = 0) -> int:
-    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups, rows_per_wave)
+                         kv_groups: int = 0, rows_per_wave: int = 0, stream_waves: int = 0) -> int:
+    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups, rows_per_wave, stream_waves)
     n = lib().tt_block_attn_workspace_bytes(batch, prefix_len, block_len, n_q_heads, n_kv_heads,
                                             head_dim, _dtype_code(dtype), ctypes.byref(opts))
     if n == SIZE_MAX:
@@ -157,7 +157,7 @@ def attn_workspace_bytes(batch, prefix_len, block_len, n_q_heads, n_kv_heads, he
 
 def block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, *, out=None, out_dtype=None,
                path: str = "auto", kv_splits: int = 0, kv_groups: int = 0, rows_per_wave: int = 0,
-               workspace=None, stream=None):
+               stream_waves: int = 0, workspace=None, stream=None):
     """Eq. (1) block attention through tt_block_attn_ex; returns ``out``.
 
     q [B,Hq,L,D]; k_ctx/v_ctx [B,Hkv,Pcap,D] (or None when prefix_len == 0);
@@ -190,9 +190,9 @@ def block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, *, out=None, ou
         out = torch.empty((B, Hq, L, D), dtype=out_dtype, device=device)
     _cuda_contig("out", out, device)
     _require(tuple(out.shape) == (B, Hq, L, D), "out must be [B, Hq, L, D]")
-    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups, rows_per_wave)
+    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups, rows_per_wave, stream_waves)
     need = attn_workspace_bytes(B, prefix_len, L, Hq, Hkv, D, q.dtype, path, kv_splits, kv_groups,
-                                rows_per_wave)
+                                rows_per_wave, stream_waves)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -220,7 +220,8 @@ def _ctx_checks(k_ctx, v_ctx, q, B, Hkv, D, device, need_rows):
 
 def block_attn_varlen(q, k_ctx, v_ctx, prefix_lens, max_prefix_len, k_blk, v_blk, scale, *,
                       out=None, out_dtype=None, path: str = "auto", kv_splits: int = 0,
-                      kv_groups: int = 0, rows_per_wave: int = 0, workspace=None, stream=None):
+                      kv_groups: int = 0, rows_per_wave: int = 0,
+                      stream_waves: int = 0, workspace=None, stream=None):
     """Eq. (1) with a prefix length per batch entry (tt_block_attn_varlen).
     ``prefix_lens`` is an int32 tensor [B] on the same GPU, every value in
     [0, max_prefix_len]."""
@@ -242,9 +243,9 @@ def block_attn_varlen(q, k_ctx, v_ctx, prefix_lens, max_prefix_len, k_blk, v_blk
         out = torch.empty((B, Hq, L, D), dtype=out_dtype, device=device)
     _cuda_contig("out", out, device)
     _require(tuple(out.shape) == (B, Hq, L, D), "out must be [B, Hq, L, D]")
-    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups, rows_per_wave)
+    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups, rows_per_wave, stream_waves)
     need = attn_workspace_bytes(B, max_prefix_len, L, Hq, Hkv, D, q.dtype, path, kv_splits,
-                                kv_groups, rows_per_wave)
+                                kv_groups, rows_per_wave, stream_waves)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -259,8 +260,9 @@ def block_attn_varlen(q, k_ctx, v_ctx, prefix_lens, max_prefix_len, k_blk, v_blk
 
 def attn_multiblock_workspace_bytes(batch, block_size, n_blocks, n_q_heads, n_kv_heads, head_dim,
                                     dtype: torch.dtype, path: str = "auto", kv_splits: int = 0,
-                                    kv_groups: int = 0, rows_per_wave: int = 0) -> int:
-    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups, rows_per_wave)
+                                    kv_groups: int = 0, rows_per_wave: int = 0,
+                                    stream_waves: int = 0) -> int:
+    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups, rows_per_wave, stream_waves)
     n = lib().tt_block_attn_multiblock_workspace_bytes(batch, block_size, n_blocks, n_q_heads,
                                                        n_kv_heads, head_dim, _dtype_code(dtype),
                                                        ctypes.byref(opts))
@@ -271,7 +273,8 @@ def attn_multiblock_workspace_bytes(batch, block_size, n_blocks, n_q_heads, n_kv
 
 def block_attn_multiblock(q, k_ctx, v_ctx, k_noisy, v_noisy, block_size, scale, *, out=None,
                           out_dtype=None, path: str = "auto", kv_splits: int = 0,
-                          kv_groups: int = 0, rows_per_wave: int = 0, workspace=None, stream=None):
+                          kv_groups: int = 0, rows_per_wave: int = 0,
+                          stream_waves: int = 0, workspace=None, stream=None):
     """Training-style pass over all noisy blocks (tt_block_attn_multiblock).
     q [B,Hq,N*S,D]; k_ctx/v_ctx [B,Hkv,cap,D] with cap >= (N-1)*S;
     k_noisy/v_noisy [B,Hkv,N*S,D]."""
@@ -294,9 +297,9 @@ def block_attn_multiblock(q, k_ctx, v_ctx, k_noisy, v_noisy, block_size, scale, 
         out = torch.empty((B, Hq, T, D), dtype=out_dtype, device=device)
     _cuda_contig("out", out, device)
     _require(tuple(out.shape) == (B, Hq, T, D), "out must be [B, Hq, N*S, D]")
-    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups, rows_per_wave)
+    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups, rows_per_wave, stream_waves)
     need = attn_multiblock_workspace_bytes(B, S, N, Hq, Hkv, D, q.dtype, path, kv_splits,
-                                           kv_groups, rows_per_wave)
+                                           kv_groups, rows_per_wave, stream_waves)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -416,21 +419,22 @@ class Prepared:
 
 def prepare_block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, out, *,
                        path: str = "auto", kv_splits: int = 0, kv_groups: int = 0,
-                       rows_per_wave: int = 0, workspace=None, stream=None):
+                       rows_per_wave: int = 0, stream_waves: int = 0, workspace=None, stream=None):
     """Validate once (same checks as block_attn) and return a Prepared call."""
     device = q.device
     B, Hq, L, D = q.shape
     Hkv = k_blk.shape[1]
     Pcap = 0 if k_ctx is None else k_ctx.shape[2]
     need = attn_workspace_bytes(B, prefix_len, L, Hq, Hkv, D, q.dtype, path, kv_splits, kv_groups,
-                                rows_per_wave)
+                                rows_per_wave, stream_waves)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
     # one validating call through the checked path
     block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, out=out, path=path,
                kv_splits=kv_splits, kv_groups=kv_groups, rows_per_wave=rows_per_wave,
+               stream_waves=stream_waves,
                workspace=workspace, stream=stream)
-    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups, rows_per_wave)
+    opts = AttnOpts(_PATHS[path], kv_splits, kv_groups, rows_per_wave, stream_waves)
     ws_bytes = 0 if workspace is None else workspace.numel()
     args = (_ptr(q), _ptr(k_ctx), _ptr(v_ctx), prefix_len, _ptr(k_blk), _ptr(v_blk), L, Hq, Hkv,
             D, float(scale), _ptr(out), B, Pcap, _dtype_code(q.dtype), _dtype_code(out.dtype),

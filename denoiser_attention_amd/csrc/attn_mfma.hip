@@ -73,8 +73,6 @@ struct Lay {
   static constexpr int STAGE_B = 2 * TILE_B; // K tile then V tile
   static constexpr int DS = D / 16;          // MFMA k-steps over head_dim
   static constexpr int DB = D / 32;          // 32-wide blocks of output columns
-  static constexpr int LOADS = BN * CH / kThreads;  // 16-byte loads per thread per tile (K or V)
-  static_assert(BN * CH % kThreads == 0, "tile chunks must divide evenly");
   // Swizzle: chunk c of row r lives in slot c ^ f(r).
   // K is read as 16 rows x one chunk per 16 lanes: f_k spreads 16 rows over all banks.
   __device__ static int fk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
@@ -120,9 +118,9 @@ __device__ __forceinline__ float pair_max(float x) {
 // Marks a register value as used (forces its load to complete here).
 __device__ __forceinline__ void consume(bf16x8 v) { asm volatile("" ::"v"(v)); }
 
-template <int D, int NS>
+template <int PER_TILE, int NS>
 __device__ __forceinline__ void wait_tiles(int n_after) {
-  constexpr int per = 2 * Lay<D>::LOADS;
+  constexpr int per = PER_TILE;
   static_assert(NS >= 3 && NS - 3 <= 3, "ring depth outside the waits below");
   switch (n_after) {
     case 0: wait_vmcnt<0>(); break;
@@ -145,17 +143,28 @@ __device__ __forceinline__ void wait_tiles(int n_after) {
 // independent score chains), halving the LDS traffic, the tile loads and the
 // barriers per unit of matrix work; one wave per SIMD, with the output
 // accumulators in the accumulation registers.
-template <int D, int NS, int KG, int RB, bool OUT_BF16, bool POS_SCALE>
-__global__ __launch_bounds__(kThreads * KG, RB == 2 ? 1 : 2 / KG)
+// RG = 2 (KG = 1, RB = 1 only): eight waves (256 query rows) share one ring, so
+// each K/V tile fetched into LDS feeds twice the matrix work: half the
+// global-to-LDS traffic, load instructions and LDS writes per unit of work.
+// One such workgroup per CU (two waves per SIMD).
+template <int D, int NS, int KG, int RB, int RG, bool OUT_BF16, bool POS_SCALE>
+__global__ __launch_bounds__(kThreads * KG * RG, RB == 2 ? 1 : 2 / (KG * RG))
 void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   using L = Lay<D>;
   static_assert(RB == 1 || (RB == 2 && KG == 1), "64-row waves use one key group");
-  constexpr int WBM = 32 * RB * kWaves;   // packed query rows per group
-  __shared__ __attribute__((aligned(1024))) char smem_all[KG * NS * L::STAGE_B];
+  static_assert(RG == 1 || (RG == 2 && KG == 1 && RB == 1), "shared streams use one key group");
+  constexpr int NW = kWaves * RG;         // waves sharing one ring
+  constexpr int NT = 64 * NW;             // threads filling one ring
+  constexpr int LOADS = L::CH * BN / NT;  // 16-byte loads per thread per tile (K or V)
+  static_assert(L::CH * BN % NT == 0 && LOADS >= 1, "tile chunks must divide evenly");
+  constexpr int WBM = 32 * RB * NW;       // packed query rows per group
+  constexpr int RING_B = KG * NS * L::STAGE_B;
+  constexpr int STAGE_OUT_B = NW * 32 * D * 4;   // fp32 output staging (RG = 2)
+  __shared__ __attribute__((aligned(1024))) char smem_all[RG == 2 && STAGE_OUT_B > RING_B ? STAGE_OUT_B : RING_B];
 
   const int gtid = threadIdx.x;
   const int kgrp = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane(gtid >> 8);  // key group
-  const int tid = gtid & (kThreads - 1);                    // thread index within the group
+  const int tid = KG == 1 ? gtid : gtid & (kThreads - 1);   // thread index within the group
   char* const smem = smem_all + kgrp * NS * L::STAGE_B;     // this group's ring
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave within the group
@@ -225,11 +234,11 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // the tile that straddles the two (or runs past the end) computes each row's
   // address, with rows past the end loading the last valid row (their scores
   // are masked).
-  uint32_t koff[L::LOADS], voff[L::LOADS];
-  int rrow[L::LOADS];
+  uint32_t koff[LOADS], voff[LOADS];
+  int rrow[LOADS];
 #pragma unroll
-  for (int i = 0; i < L::LOADS; ++i) {
-    const int s = i * kThreads + tid;
+  for (int i = 0; i < LOADS; ++i) {
+    const int s = i * NT + tid;
     const int r = s / L::CH, q = s % L::CH;
     rrow[i] = r;
     koff[i] = r * L::ROWB + ((q ^ L::fk(r)) << 4);
@@ -252,8 +261,8 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
       kbase = vbase = nullptr;
     }
 #pragma unroll
-    for (int i = 0; i < L::LOADS; ++i) {
-      const uint32_t wofs = (i * kThreads + wave * 64) * 16;   // wave-uniform destination
+    for (int i = 0; i < LOADS; ++i) {
+      const uint32_t wofs = (i * NT + wave * 64) * 16;   // wave-uniform destination
       if (uniform) {
         dma16_s(kbase, koff[i], kst + wofs);
         dma16_s(vbase, voff[i], vst + wofs);
@@ -430,7 +439,7 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // same number of these (and so of barriers), also past the end of its
   // group's tiles.
   auto advance = [&](int i) {
-    wait_tiles<D, NS>(max(0, min(NS - 3, cnt - 1 - i)));
+    wait_tiles<2 * LOADS, NS>(max(0, min(NS - 3, cnt - 1 - i)));
     barrier();
     if (i + NS - 2 < cnt) issue(t_begin + i + NS - 2, slot_of(i + NS - 2));
   };
@@ -572,7 +581,7 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     stg = reinterpret_cast<float*>(smem_all) + wave * 32 * D;
   }
   static_assert(32 * D <= (L::DB * 16 + 2) * 64, "staging tile fits the exchange area");
-  static_assert(kWaves * 32 * D * 4 <= NS * L::STAGE_B, "staging tiles fit the ring");
+  static_assert(NW * 32 * D * 4 <= sizeof(smem_all), "staging tiles fit the ring");
   if (!wave_active) return;
   const size_t rows_total = (size_t)p.B * p.NB * p.Hq * p.L;
 #pragma unroll
@@ -638,23 +647,27 @@ constexpr int kStages = 4;
 
 template <int D, bool OUT_BF16, bool POS>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
-  const int rows_wg = p.rows_per_wave == 64 ? 2 * BM : BM;
+  const int rows_wg = (p.rows_per_wave == 64 || p.stream_waves == 8) ? 2 * BM : BM;
   const int m_tiles = (p.M + rows_wg - 1) / rows_wg;
   const long long n = (long long)m_tiles * p.splits * p.B * p.NB * p.Hkv;
   if (n <= 0 || n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (p.rows_per_wave == 64) {
+  if (p.rows_per_wave == 64 || p.stream_waves == 8) {
     if constexpr (D == 128) {
-      if (p.kgroups != 1) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, 2, OUT_BF16, POS>), dim3((unsigned)n),
-                         dim3(kThreads), 0, stream, p, m_tiles, (int)n);
+      if (p.kgroups != 1 || (p.rows_per_wave == 64 && p.stream_waves == 8)) return hipErrorInvalidValue;
+      if (p.rows_per_wave == 64)
+        hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, 2, 1, OUT_BF16, POS>), dim3((unsigned)n),
+                           dim3(kThreads), 0, stream, p, m_tiles, (int)n);
+      else
+        hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, 1, 2, OUT_BF16, POS>), dim3((unsigned)n),
+                           dim3(2 * kThreads), 0, stream, p, m_tiles, (int)n);
     } else {
       return hipErrorInvalidValue;
     }
   } else if (p.kgroups == 2) {
-    hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 2, 1, OUT_BF16, POS>), dim3((unsigned)n),
+    hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 2, 1, 1, OUT_BF16, POS>), dim3((unsigned)n),
                        dim3(2 * kThreads), 0, stream, p, m_tiles, (int)n);
   } else {
-    hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, 1, OUT_BF16, POS>), dim3((unsigned)n),
+    hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, 1, 1, OUT_BF16, POS>), dim3((unsigned)n),
                        dim3(kThreads), 0, stream, p, m_tiles, (int)n);
   }
   return hipGetLastError();

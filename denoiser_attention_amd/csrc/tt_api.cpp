@@ -41,6 +41,7 @@ struct AttnPlan {
   int path = TT_ATTN_SHUFFLE;  // resolved family
   int kgroups = 1;             // MFMA: wave groups splitting a workgroup's keys
   int rows_per_wave = 32;      // MFMA: query rows per wavefront
+  int stream_waves = 4;        // MFMA: waves sharing one K/V tile stream
   int splits = 1;
   int tiles_per_split = 1;
   bool empty = false;          // nothing to compute
@@ -64,6 +65,8 @@ tt_status plan_attn(long long B, int P, int L, int Hq, int Hkv, int D, tt_dtype 
   if (opts && opts->kv_splits < 0) return TT_EINVAL;
   if (opts && (opts->kv_groups < 0 || opts->kv_groups > 2)) return TT_EINVAL;
   if (opts && opts->rows_per_wave != 0 && opts->rows_per_wave != 32 && opts->rows_per_wave != 64)
+    return TT_EINVAL;
+  if (opts && opts->stream_waves != 0 && opts->stream_waves != 4 && opts->stream_waves != 8)
     return TT_EINVAL;
   if ((long long)P + L > INT_MAX / 2) return TT_EUNSUPPORTED;
   const int G = Hq / Hkv;
@@ -109,9 +112,17 @@ tt_status plan_attn(long long B, int P, int L, int Hq, int Hkv, int D, tt_dtype 
     const bool rows64 = req_rows == 64;
     if (rows64 && (D != 128 || req_groups == 2)) return TT_EUNSUPPORTED;
     plan->rows_per_wave = rows64 ? 64 : 32;
-    const long long base = rows64 ? base64 : cdiv(M, tt::kAttnMfmaBM) * B * Hkv;
-    const long long target = rows64 ? kMfmaTargetWG / 2 : kMfmaTargetWG;
-    plan->kgroups = rows64 ? 1 : (req_groups ? req_groups : (base >= kMfmaTargetWG ? 1 : 2));
+    // Eight waves (256 rows) sharing one K/V stream halve the tile loads per
+    // unit of matrix work; they need enough query tiles to fill the chip with
+    // one such workgroup per CU.
+    const int req_sw = opts ? opts->stream_waves : 0;
+    if (req_sw == 8 && (D != 128 || rows64 || req_groups == 2)) return TT_EUNSUPPORTED;
+    const long long base128 = cdiv(M, tt::kAttnMfmaBM) * B * Hkv;
+    const bool sw8 = req_sw == 8;
+    plan->stream_waves = sw8 ? 8 : 4;
+    const long long base = (rows64 || sw8) ? base64 : base128;
+    const long long target = (rows64 || sw8) ? kMfmaTargetWG / 2 : kMfmaTargetWG;
+    plan->kgroups = (rows64 || sw8) ? 1 : (req_groups ? req_groups : (base >= kMfmaTargetWG ? 1 : 2));
     if (opts && opts->kv_splits > 0) {
       splits = opts->kv_splits < n_tiles ? opts->kv_splits : n_tiles;
     } else {
@@ -264,6 +275,7 @@ tt_status attn_run(const AttnCall& c) {
   p.tiles_per_split = plan.tiles_per_split;
   p.kgroups = plan.kgroups;
   p.rows_per_wave = plan.rows_per_wave;
+  p.stream_waves = plan.stream_waves;
   p.out_bf16 = c.out_dtype == TT_BF16 ? 1 : 0;
   p.scale_log2 = c.scale * kLog2e;
   if (plan.splits > 1) {

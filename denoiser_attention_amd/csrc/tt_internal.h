@@ -43,6 +43,8 @@ struct AttnParams {
   int tiles_per_split; // key tiles handled by one split
   int kgroups;         // MFMA kernel: 1 or 2 key groups inside a workgroup
   int rows_per_wave;   // MFMA kernel: 32, or 64 (head_dim 128, one key group)
+  int stream_waves;    // MFMA kernel: waves sharing one K/V stream, 4 or 8 (head_dim 128,
+                       // one key group, 32-row waves)
   int out_bf16;        // 1: write bf16 output, 0: fp32
   float scale_log2;    // softmax scale * log2(e)
 };

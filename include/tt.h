@@ -67,12 +67,17 @@ typedef enum { TT_ATTN_AUTO = 0, TT_ATTN_MFMA = 1, TT_ATTN_SHUFFLE = 2 } tt_attn
  * workgroup's key range between them (merged on chip).  rows_per_wave (MFMA
  * kernel only) = 0 lets the library choose, 32 or 64 forces how many query rows
  * one wavefront owns; 64 needs head_dim 128 and one wave group (otherwise
- * TT_EUNSUPPORTED). */
+ * TT_EUNSUPPORTED).  stream_waves (MFMA kernel only) = 0 lets the library
+ * choose, 4 or 8 forces how many wavefronts of a workgroup share one stream of
+ * K/V tiles through LDS (8: 256 query rows per workgroup, half the tile loads
+ * per unit of work; needs head_dim 128, one wave group and 32-row waves,
+ * otherwise TT_EUNSUPPORTED).  Values outside these sets give TT_EINVAL. */
 typedef struct {
   int path;           /* tt_attn_path */
   int kv_splits;      /* 0 = auto */
   int kv_groups;      /* 0 = auto, 1 or 2 */
   int rows_per_wave;  /* 0 = auto, 32 or 64 */
+  int stream_waves;   /* 0 = auto, 4 or 8 */
 } tt_attn_opts;
 
 /* Human-readable name of a status code (static storage, never NULL). */

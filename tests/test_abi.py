@@ -64,6 +64,7 @@ def attn_call(**kw):
     dict(dtype=7), dict(odt=7), dict(dtype=B.TT_FP32, odt=B.TT_BF16),
     dict(opts=(9, 0, 0)), dict(opts=(0, -1, 0)), dict(opts=(0, 0, 3)), dict(opts=(0, 0, -1)),
     dict(opts=(0, 0, 0, 48)), dict(opts=(0, 0, 0, -32)),
+    dict(opts=(0, 0, 0, 0, 6)), dict(opts=(0, 0, 0, 0, -8)),
     # bf16 with a split that needs a workspace, none given
     dict(dtype=B.TT_BF16, odt=B.TT_BF16, hq=32, hkv=2, d=128, prefix_len=2048, pcap=2048,
          block_len=32, batch=8, opts=(B.TT_ATTN_MFMA, 4, 0)),
@@ -78,6 +79,10 @@ def test_attn_rejects_invalid(kw):
     # 64-row waves: head_dim 128 and one wave group only
     dict(dtype=B.TT_BF16, odt=B.TT_BF16, d=64, opts=(B.TT_ATTN_MFMA, 0, 0, 64)),
     dict(dtype=B.TT_BF16, odt=B.TT_BF16, d=128, opts=(B.TT_ATTN_MFMA, 0, 2, 64)),
+    # eight waves on one K/V stream: head_dim 128, one wave group, 32-row waves only
+    dict(dtype=B.TT_BF16, odt=B.TT_BF16, d=64, opts=(B.TT_ATTN_MFMA, 0, 0, 0, 8)),
+    dict(dtype=B.TT_BF16, odt=B.TT_BF16, d=128, opts=(B.TT_ATTN_MFMA, 0, 2, 0, 8)),
+    dict(dtype=B.TT_BF16, odt=B.TT_BF16, d=128, opts=(B.TT_ATTN_MFMA, 0, 0, 64, 8)),
 ])
 def test_attn_unsupported(kw):
     assert attn_call(**kw) == B.TT_EUNSUPPORTED

@@ -121,6 +121,36 @@ def test_rows64_matches_rows32_closely():
     check_attn(b, ref, "bf16", False, "rows32")
 
 
+@pytest.mark.parametrize("shape", ROWS64, ids=[str(s) for s in ROWS64])
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_bf16_stream8(shape, out_f32):
+    """Eight waves (256 rows) on one K/V stream: ragged row tiles leave whole
+    waves without rows, split keys go through the merge pass."""
+    B, Hq, Hkv, L, P, Pcap, splits = shape
+    cfg = small_cfg(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=128, prefix_len=P, block_len=L)
+    inp = synth.attn_inputs(cfg, seed=10, prefix_cap=Pcap)
+    if Pcap == 0:
+        inp["k_ctx"] = inp["k_ctx"].reshape(B, Hkv, 0, 128)
+    kw = dict(path="mfma", stream_waves=8, kv_splits=splits)
+    if out_f32:
+        kw["out_dtype"] = torch.float32
+    got = gpu_attn(inp, DEV, **kw)
+    check_attn(got, oracle_attn(inp), "bf16", not out_f32, f"stream8 {shape} f32out={out_f32}")
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_stream8_bitwise_equals_stream4(splits):
+    """Sharing the tile stream changes which waves load a tile, not any wave's
+    arithmetic: the outputs are bit-identical to four-wave workgroups."""
+    cfg = small_cfg(batch=2, prefix_len=613, block_len=45)
+    inp = synth.attn_inputs(cfg, seed=11)
+    a = gpu_attn(inp, DEV, path="mfma", kv_groups=1, stream_waves=8, kv_splits=splits,
+                 out_dtype=torch.float32)
+    b = gpu_attn(inp, DEV, path="mfma", kv_groups=1, stream_waves=4, kv_splits=splits,
+                 out_dtype=torch.float32)
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
 def test_paths_agree_and_deterministic():
     cfg = small_cfg(batch=2, prefix_len=257, block_len=32)
     inp = synth.attn_inputs(cfg, seed=4)

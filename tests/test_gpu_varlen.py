@@ -89,6 +89,14 @@ def test_varlen_rows64(splits):
     check_attn(got, oracle_varlen(inp), "bf16", False, f"varlen rows64 splits={splits}")
 
 
+@pytest.mark.parametrize("splits", [0, 2])
+def test_varlen_stream8(splits):
+    cfg = base_cfg(batch=5, block_len=40)
+    inp = synth.varlen_inputs(cfg, seed=17, max_prefix_len=400, prefix_cap=410)
+    got = gpu_varlen(inp, path="mfma", stream_waves=8, kv_splits=splits, out_dtype=torch.float32)
+    check_attn(got, oracle_varlen(inp), "bf16", False, f"varlen stream8 splits={splits}")
+
+
 def test_varlen_fp32():
     cfg = synth.get_config("tiny_fp32")
     inp = synth.varlen_inputs(cfg, seed=13, batch=4, max_prefix_len=53, prefix_cap=70)
@@ -186,6 +194,14 @@ def test_multiblock_rows64(splits):
     inp = synth.multiblock_inputs(cfg, 5, 40, seed=25)
     got = gpu_multiblock(inp, path="mfma", rows_per_wave=64, kv_splits=splits)
     check_attn(got, oracle_multiblock(inp), "bf16", True, f"multiblock rows64 splits={splits}")
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_multiblock_stream8(splits):
+    cfg = base_cfg(batch=2, n_q_heads=16, n_kv_heads=2)
+    inp = synth.multiblock_inputs(cfg, 5, 40, seed=26)
+    got = gpu_multiblock(inp, path="mfma", stream_waves=8, kv_splits=splits)
+    check_attn(got, oracle_multiblock(inp), "bf16", True, f"multiblock stream8 splits={splits}")
 
 
 def test_multiblock_fp32():
