@@ -12,22 +12,25 @@
 //   lmhead_rows_kernel   -- one workgroup: the masked positions, in order,
 //                           and their count (committed positions are never
 //                           projected).
-//   lmhead_stats_kernel  -- one workgroup per (128 masked rows, 256-entry
-//                           vocabulary slice).  Computes S^T = W_slice . H^T
-//                           with v_mfma_f32_32x32x16_bf16 (A = 32 vocabulary
-//                           rows, B = 32 hidden rows, both read as 16-byte
-//                           runs along d_model), so that in the accumulator
-//                           layout each lane owns one hidden row and 16 of a
-//                           tile's 32 vocabulary entries: the per-row
-//                           statistics are formed inside the lane, then with
-//                           lane ^ 32, then across the 4 waves through LDS.
-//                           Wave w covers vocabulary entries 64w..64w+63 of
-//                           the slice against all 128 rows (8 accumulator
+//   lmhead_stats_kernel  -- one workgroup of 8 waves per (256 masked rows,
+//                           256-entry vocabulary slice).  Computes S^T =
+//                           W_slice . H^T with v_mfma_f32_32x32x16_bf16 (A =
+//                           32 vocabulary rows, B = 32 hidden rows, both read
+//                           as 16-byte runs along d_model), so that in the
+//                           accumulator layout each lane owns one hidden row
+//                           and 16 of a tile's 32 vocabulary entries: the
+//                           per-row statistics are formed inside the lane,
+//                           then with lane ^ 32, then across the 4 vocabulary
+//                           waves of its row half through LDS.  Wave w covers
+//                           vocabulary entries 64(w%4)..+63 of the slice
+//                           against rows 128(w/4)..+127 (8 accumulator
 //                           tiles).  W and H tiles of 32 d_model columns
-//                           stream into a 3-stage LDS ring (72 KB, so two
-//                           workgroups share a CU) with 16-byte direct-to-LDS
+//                           stream into a 4-stage LDS ring (128 KB, one
+//                           workgroup per CU) with 16-byte direct-to-LDS
 //                           loads (rows XOR-swizzled at 16-byte granularity);
-//                           2 stages are in flight while one is consumed.
+//                           3 stages are in flight while one is consumed, so
+//                           the weight stream from HBM has about 1.5 us of
+//                           lead, and each weight tile feeds 256 rows.
 //   lmhead_merge_kernel  -- one wavefront per masked row: merges the row's
 //                           slice partials into one.
 // The confidence-ranking and commit step then runs on the merged partials.
@@ -43,18 +46,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                          // 4 vocabulary ranges x 2 row halves
 constexpr int kThreads = 64 * kWaves;
-constexpr int NS = 3;                               // ring stages (2 workgroups per CU)
+constexpr int NS = 4;                               // ring stages (one workgroup per CU)
 constexpr int ROWB = kLmK * 2;                      // bytes of one row of a stage (64)
 constexpr int W_TILE = kLmVocab * ROWB;             // 16 KB
-constexpr int H_TILE = kLmRows * ROWB;              // 8 KB
-constexpr int STAGE = W_TILE + H_TILE;              // 24 KB
-constexpr int W_LOADS = W_TILE / 16 / kThreads;     // 4 direct loads per thread
+constexpr int H_TILE = kLmRows * ROWB;              // 16 KB
+constexpr int STAGE = W_TILE + H_TILE;              // 32 KB
+constexpr int W_LOADS = W_TILE / 16 / kThreads;     // 2 direct loads per thread
 constexpr int H_LOADS = H_TILE / 16 / kThreads;     // 2
 constexpr int PER_STAGE = W_LOADS + H_LOADS;        // vector-memory ops per stage
-static_assert(kLmVocab == 64 * kWaves, "one 64-entry vocabulary range per wave");
-static_assert(kLmRows == 128 && kLmK == 32, "tile shape");
+static_assert(kLmVocab == 64 * 4, "four 64-entry vocabulary ranges per workgroup");
+static_assert(kLmRows == 256 && kLmK == 32, "tile shape");
 static_assert(NS * STAGE <= 160 * 1024, "ring fits the LDS");
 
 // Chunk q (16 bytes) of stage row r lives in slot q ^ f(r): eight consecutive
@@ -135,11 +138,12 @@ __global__ __launch_bounds__(1024) void lmhead_rows_kernel(LmParams p) {
   if (tid == 0) *p.n_rows = s_base;
 }
 
-__global__ __launch_bounds__(kThreads, 2) void lmhead_stats_kernel(LmParams p, int n_rt) {
+__global__ __launch_bounds__(kThreads, 1) void lmhead_stats_kernel(LmParams p, int n_rt) {
   __shared__ __attribute__((aligned(1024))) char ring[NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int vw = wave & 3, rw = wave >> 2;         // vocabulary range, row half
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int rt = logical % n_rt, slice = logical / n_rt;
   const int n_rows = *p.n_rows;
@@ -179,14 +183,15 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_stats_kernel(LmParams p, i
       dma16_s(hk, hoff[j], st + W_TILE + (kThreads * j + wave * 64) * 16);
   };
 
-  // Operand rows of this lane: vocabulary rows 64*wave + 32*vt + (lane & 31),
-  // hidden rows 32*rt + (lane & 31); the lane half picks the 8-column run.
+  // Operand rows of this lane: vocabulary rows 64*vw + 32*vt + (lane & 31),
+  // hidden rows 128*rw + 32*t + (lane & 31); the lane half picks the 8-column
+  // run.
   const int lr = lane & 31, hh = lane >> 5;
   int a_row[2], b_row[4];
 #pragma unroll
-  for (int vt = 0; vt < 2; ++vt) a_row[vt] = 64 * wave + 32 * vt + lr;
+  for (int vt = 0; vt < 2; ++vt) a_row[vt] = 64 * vw + 32 * vt + lr;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) b_row[t] = 32 * t + lr;
+  for (int t = 0; t < 4; ++t) b_row[t] = 128 * rw + 32 * t + lr;
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -229,9 +234,9 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_stats_kernel(LmParams p, i
   }
 
   // Statistics of each hidden row over this wave's 64 entries.  Accumulator
-  // register r of tile (vt, t) holds entry 64*wave + 32*vt + 8*(r/4) +
-  // 4*hh + r%4 of row 32*t + lr; they are visited in increasing id order, so
-  // a strict '>' keeps the lowest id among equal maxima.
+  // register r of tile (vt, t) holds entry 64*vw + 32*vt + 8*(r/4) + 4*hh +
+  // r%4 of row 128*rw + 32*t + lr; they are visited in increasing id order,
+  // so a strict '>' keeps the lowest id among equal maxima.
   Triple tr[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -241,7 +246,7 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_stats_kernel(LmParams p, i
     for (int vt = 0; vt < 2; ++vt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int v = vocab0 + 64 * wave + 32 * vt + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int v = vocab0 + 64 * vw + 32 * vt + 8 * (r >> 2) + 4 * hh + (r & 3);
         if (v < p.V && acc[vt][t][r] > m) {
           m = acc[vt][t][r];
           arg = v;
@@ -254,25 +259,26 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_stats_kernel(LmParams p, i
       for (int vt = 0; vt < 2; ++vt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int v = vocab0 + 64 * wave + 32 * vt + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int v = vocab0 + 64 * vw + 32 * vt + 8 * (r >> 2) + 4 * hh + (r & 3);
           if (v < p.V) s += __builtin_amdgcn_exp2f(fmaf(acc[vt][t][r], kLog2e, -mb));
         }
     }
     tr[t] = combine(Triple{m, arg, s}, shfl_xor_triple(Triple{m, arg, s}, 32));
   }
 
-  // Across the 4 waves (LDS; the ring is free once every wave is past it).
+  // Across the 4 vocabulary ranges (LDS; the ring is free once every wave is
+  // past it).
   barrier();
-  Triple* xt = reinterpret_cast<Triple*>(ring);   // [wave][128 rows]
+  Triple* xt = reinterpret_cast<Triple*>(ring);   // [vocabulary range][256 rows]
   if (hh == 0) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) xt[wave * kLmRows + 32 * t + lr] = tr[t];
+    for (int t = 0; t < 4; ++t) xt[vw * kLmRows + 128 * rw + 32 * t + lr] = tr[t];
   }
   __syncthreads();
   if (tid < rows_here) {
     Triple r = xt[tid];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = combine(r, xt[w * kLmRows + tid]);
+    for (int w = 1; w < 4; ++w) r = combine(r, xt[w * kLmRows + tid]);
     const int row = p.row_ids[row0 + tid];
     VocabPartial out;
     out.m = r.m;

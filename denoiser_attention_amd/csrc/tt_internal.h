@@ -148,7 +148,7 @@ hipError_t launch_vocab_reduce(const UnmaskParams& p, hipStream_t stream);
 hipError_t launch_topk_commit(const UnmaskParams& p, hipStream_t stream);
 
 // Fused LM-head projection + vocabulary statistics.
-constexpr int kLmRows = 128;     // hidden rows per workgroup
+constexpr int kLmRows = 256;     // hidden rows per workgroup
 constexpr int kLmVocab = 256;    // vocabulary entries per workgroup (one slice)
 constexpr int kLmK = 32;         // d_model per pipeline stage
 struct LmParams {
