@@ -11,8 +11,9 @@
 //   (32 KB) chunk of one masked row: every thread issues all of its 128-bit
 //   loads up front (8 x 16 B), takes the max / lowest-id argmax over its 32
 //   values on the raw fp32 logits, then its sum of exp2((x - max) * log2 e);
-//   the (max, argmax, sum) triples are merged across the wave with xor
-//   shuffles and across the 4 waves through LDS, ties going to the lower id at
+//   across the wave the maximum is found first (xor shuffles), then the lowest
+//   id attaining it and the sum rescaled once to it; the 4 waves' (max,
+//   argmax, sum) triples merge through LDS, ties going to the lower id at
 //   every stage.  Chunks of unmasked rows exit at once.
 // topk_commit_kernel -- one workgroup per sequence: merges the chunk triples of
 //   each masked position (one thread per position, in chunk order), forms the
@@ -53,14 +54,6 @@ __device__ __forceinline__ Triple combine(Triple a, Triple b) {
   r.s = sa + sb;
   r.arg = a.m > b.m ? a.arg : (b.m > a.m ? b.arg : min(a.arg, b.arg));
   return r;
-}
-
-__device__ __forceinline__ Triple shfl_xor_triple(Triple t, int mask) {
-  Triple o;
-  o.m = __shfl_xor(t.m, mask);
-  o.arg = __shfl_xor(t.arg, mask);
-  o.s = __shfl_xor(t.s, mask);
-  return o;
 }
 
 template <bool VEC>
@@ -124,8 +117,21 @@ __global__ __launch_bounds__(kThreads) void vocab_reduce_kernel(UnmaskParams p) 
     }
   }
 
+  // Across the wave: the maximum first, then the lowest id attaining it and
+  // the sum rescaled once to that maximum (one exponential per lane).
+  {
+    float m = t.m;
 #pragma unroll
-  for (int mask = 32; mask >= 1; mask >>= 1) t = combine(t, shfl_xor_triple(t, mask));
+    for (int mask = 32; mask >= 1; mask >>= 1) m = fmaxf(m, __shfl_xor(m, mask));
+    int arg = t.m == m ? t.arg : INT_MAX;
+    float s = t.m == -INFINITY ? 0.0f : t.s * __builtin_amdgcn_exp2f((t.m - m) * kLog2e);
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) {
+      arg = min(arg, __shfl_xor(arg, mask));
+      s += __shfl_xor(s, mask);
+    }
+    t = Triple{m, arg, s};
+  }
 
   __shared__ Triple s_t[kThreads / 64];
   const int lane = tid & 63, wave = tid >> 6;
