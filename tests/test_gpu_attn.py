@@ -6,7 +6,7 @@ import pytest
 import torch
 
 from denoiser_attention_amd import synth
-from helpers import check_attn, gpu_attn, oracle_attn, say, to_dev
+from helpers import as_f64, check_attn, gpu_attn, oracle_attn, say, to_dev
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -149,6 +149,40 @@ def test_stream8_bitwise_equals_stream4(splits):
     b = gpu_attn(inp, DEV, path="mfma", kv_groups=1, stream_waves=4, kv_splits=splits,
                  out_dtype=torch.float32)
     assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+# Softmax scales other than 1/sqrt(D): zero (uniform weights: the output is the
+# mean of the visible V rows), negative (the kernels' other max-tracking
+# instantiation), and large (near one-hot weights that exercise the lazy
+# reference-max refresh on every tile).
+SCALES = [0.0, -0.09, 0.5, 2.0]
+
+
+@pytest.mark.parametrize("scale", SCALES)
+@pytest.mark.parametrize("path", ["mfma", "shuffle"])
+def test_scale_variants(scale, path):
+    cfg = small_cfg(batch=2, n_q_heads=8, n_kv_heads=2, prefix_len=150, block_len=37)
+    inp = synth.attn_inputs(cfg, seed=12, prefix_cap=160)
+    inp["scale"] = scale
+    got = gpu_attn(inp, DEV, path=path, out_dtype=torch.float32)
+    ref = oracle_attn(inp)
+    check_attn(got, ref, "bf16", False, f"scale={scale} {path}")
+    if scale == 0.0:
+        # closed form: every query row returns the mean of its KV head's rows
+        v = np.concatenate([inp["v_ctx"][:, :, :150], inp["v_blk"]], axis=2)
+        mean = as_f64(v).mean(axis=2)                       # [B, Hkv, D]
+        G = 8 // 2
+        want = np.repeat(mean, G, axis=1)[:, :, None, :]    # [B, Hq, 1, D]
+        assert np.abs(got - want).max() < 2e-3
+
+
+@pytest.mark.parametrize("scale", [-0.09, 2.0])
+def test_scale_variants_fp32(scale):
+    cfg = synth.get_config("tiny_fp32")
+    inp = synth.attn_inputs(cfg, seed=13, prefix_len=53, prefix_cap=70, block_len=13)
+    inp["scale"] = scale
+    got = gpu_attn(inp, DEV)
+    check_attn(got, oracle_attn(inp), "fp32", False, f"fp32 scale={scale}")
 
 
 def test_paths_agree_and_deterministic():
