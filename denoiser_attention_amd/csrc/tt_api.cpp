@@ -237,7 +237,8 @@ tt_status attn_run(const AttnCall& c) {
                            c.opts, &plan);
   if (st != TT_OK) return st;
   if (c.Pcap < Pmax) return TT_EINVAL;
-  if (!std::isfinite(c.scale)) return TT_EINVAL;
+  // The kernels work in base-2 units: scale * log2(e) must stay finite.
+  if (!std::isfinite(c.scale) || !std::isfinite(c.scale * kLog2e)) return TT_EINVAL;
   if (c.out_dtype != TT_FP32 && c.out_dtype != TT_BF16) return TT_EINVAL;
   if (c.dtype == TT_FP32 && c.out_dtype != TT_FP32) return TT_EINVAL;
   if (plan.empty) return TT_OK;

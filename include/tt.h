@@ -113,7 +113,8 @@ size_t tt_block_attn_workspace_bytes(int batch, int prefix_len, int block_len, i
  *   block_len   L >= 0 (L == 0 or batch == 0: nothing to do, TT_OK)
  *   n_q_heads, n_kv_heads  >= 1, n_q_heads a multiple of n_kv_heads
  *   head_dim    D: 64, 128 or 256 (the MFMA kernel covers 64 and 128)
- *   scale       finite multiplier of q.k (typically 1/sqrt(D))
+ *   scale       finite multiplier of q.k (typically 1/sqrt(D)); |scale| * log2(e)
+ *               must be finite too (|scale| < 2.3e38), else TT_EINVAL
  *   out    [batch, n_q_heads, block_len, head_dim]          out_dtype; must not
  *          alias any input
  *   batch       B >= 0

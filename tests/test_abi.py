@@ -61,6 +61,7 @@ def attn_call(**kw):
     dict(k_ctx=None), dict(v_ctx=None),
     dict(batch=-1), dict(block_len=-1), dict(prefix_len=-1), dict(hq=0), dict(hkv=0),
     dict(hq=6, hkv=4), dict(pcap=10), dict(scale=float("inf")), dict(scale=float("nan")),
+    dict(scale=3e38), dict(scale=-3e38),
     dict(dtype=7), dict(odt=7), dict(dtype=B.TT_FP32, odt=B.TT_BF16),
     dict(opts=(9, 0, 0)), dict(opts=(0, -1, 0)), dict(opts=(0, 0, 3)), dict(opts=(0, 0, -1)),
     dict(opts=(0, 0, 0, 48)), dict(opts=(0, 0, 0, -32)),
