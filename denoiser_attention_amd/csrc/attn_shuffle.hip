@@ -212,15 +212,36 @@ __global__ __launch_bounds__(64) void attn_shuffle_kernel(AttnParams p, int row_
 // overlap; the merge is an online (running max) combination in split order.
 constexpr int kMergeBatch = 8;
 
+// Four consecutive output columns of one row, in the output type.
+template <typename T>
+__device__ __forceinline__ void store_out4(void* out, size_t idx, f32x4 v);
+template <>
+__device__ __forceinline__ void store_out4<float>(void* out, size_t idx, f32x4 v) {
+  *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = v;
+}
+template <>
+__device__ __forceinline__ void store_out4<uint16_t>(void* out, size_t idx, f32x4 v) {
+  const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.x) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.y) << 16);
+  const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.z) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.w) << 16);
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) = make_uint2(lo, hi);
+}
+
+// One thread per (packed row, 4 columns); rows * D / 4 < 2^32 (checked at
+// launch), so the index arithmetic is 32-bit, and D / 4 is a power of two.
 template <typename TO>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
-  const size_t rows = (size_t)p.B * p.NB * p.Hq * p.L;
-  const int groups = p.D / 4;
-  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= rows * groups) return;
-  const size_t row = gid / groups;          // packed row ((item * Hkv + kvh) * M + r)
-  const int g = (int)(gid % groups);
-  const int pair = (int)(row / p.M), r = (int)(row - (size_t)pair * p.M);
+  const uint32_t rows = (uint32_t)p.B * p.NB * p.Hq * p.L;
+  const int gshift = __builtin_ctz((unsigned)(p.D / 4));
+  // Workgroups follow the attention kernel's XCD order (contiguous runs of
+  // (item, KV head) pairs per XCD), so each XCD merges partials its own L2
+  // received.
+  const uint32_t gid = (uint32_t)xcd_remap(blockIdx.x, gridDim.x) * 256u + threadIdx.x;
+  if (gid >= rows << gshift) return;
+  const uint32_t row = gid >> gshift;          // packed row ((item * Hkv + kvh) * M + r)
+  const int g = (int)(gid & ((1u << gshift) - 1));
+  const int pair = (int)(row / (uint32_t)p.M), r = (int)(row - (uint32_t)pair * p.M);
   const int w = pair / p.Hkv, kvh = pair - w * p.Hkv;
   const AttnItem it = attn_item(p, w, kvh);
   const int n_splits = attn_item_splits(p, it.n_keys);   // splits that hold keys of this item
@@ -232,9 +253,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
       if (s0 + i < n_splits) {
-        const size_t r = (size_t)(s0 + i) * rows + row;
-        lse[i] = p.part_lse[r];
-        o[i] = *reinterpret_cast<const f32x4*>(p.part_o + r * p.D + 4 * g);
+        const size_t r2 = (size_t)(s0 + i) * rows + row;
+        lse[i] = p.part_lse[r2];
+        o[i] = *reinterpret_cast<const f32x4*>(p.part_o + r2 * p.D + 4 * g);
       }
     }
 #pragma unroll
@@ -242,17 +263,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
       if (s0 + i < n_splits) {
         const float m_new = fmaxf(m, lse[i]);
         const float a = __builtin_amdgcn_exp2f(m - m_new);       // 0 on the first split
-        const float w = __builtin_amdgcn_exp2f(lse[i] - m_new);
-        wsum = wsum * a + w;
-        acc = acc * a + w * o[i];
+        const float wt = __builtin_amdgcn_exp2f(lse[i] - m_new);
+        wsum = wsum * a + wt;
+        acc = acc * a + wt * o[i];
         m = m_new;
       }
     }
   }
   const float inv = 1.0f / wsum;
-  const size_t base = (it.q_head0 + attn_row_off(p, r)) * p.D + 4 * g;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) store_out<TO>(p.out, base + i, acc[i] * inv);
+  store_out4<TO>(p.out, (it.q_head0 + attn_row_off(p, r)) * p.D + 4 * g, acc * inv);
 }
 
 template <int D, typename T, typename TO>
@@ -290,8 +309,8 @@ hipError_t launch_attn_shuffle(const AttnParams& p, int in_bf16, hipStream_t str
 
 hipError_t launch_attn_merge(const AttnParams& p, hipStream_t stream) {
   const size_t n = (size_t)p.B * p.NB * p.Hq * p.L * (p.D / 4);
+  if (n == 0 || n > 0xffffff00ULL) return hipErrorInvalidConfiguration;   // 32-bit indices
   const size_t blocks = (n + 255) / 256;
-  if (blocks == 0 || blocks > 0x7fffffffULL) return hipErrorInvalidConfiguration;
   if (p.out_bf16) {
     hipLaunchKernelGGL(attn_merge_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        p);

@@ -152,6 +152,8 @@ tt_status plan_attn(long long B, int P, int L, int Hq, int Hkv, int D, tt_dtype 
   plan->tiles_per_split = (int)tps;
   if (splits > 1) {
     const size_t rows = (size_t)B * Hq * L;
+    // The merge pass indexes (row, 4 columns) with 32-bit arithmetic.
+    if (rows * (size_t)(D / 4) > 0xffffff00ULL) return TT_EUNSUPPORTED;
     const size_t o_bytes = align_up((size_t)splits * rows * D * sizeof(float));
     plan->lse_offset = o_bytes;
     plan->ws_bytes = o_bytes + align_up((size_t)splits * rows * sizeof(float));
