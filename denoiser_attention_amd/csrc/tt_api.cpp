@@ -1,6 +1,7 @@
 // Host side of libtt: argument validation, kernel-family and split planning,
 // workspace layout, and launches on the caller's stream.  The public contract
 // is include/tt.h.  Nothing here allocates device memory.
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstddef>
@@ -121,8 +122,24 @@ tt_status plan_attn(long long B, int P, int L, int Hq, int Hkv, int D, tt_dtype 
     const bool sw8 = req_sw == 8;
     plan->stream_waves = sw8 ? 8 : 4;
     const long long base = (rows64 || sw8) ? base64 : base128;
-    const long long target = (rows64 || sw8) ? kMfmaTargetWG / 2 : kMfmaTargetWG;
-    plan->kgroups = (rows64 || sw8) ? 1 : (req_groups ? req_groups : (base >= kMfmaTargetWG ? 1 : 2));
+    // With few query tiles, two wave groups per workgroup split each key range
+    // on chip -- unless that leaves each group fewer than 8 tiles, where the
+    // pipeline start and the on-chip merge dominate: one group per workgroup
+    // and about one workgroup per CU of key splits measured faster there.
+    long long target = kMfmaTargetWG;
+    if (rows64 || sw8) {
+      plan->kgroups = 1;
+      target = kMfmaTargetWG / 2;
+    } else if (req_groups) {
+      plan->kgroups = req_groups;
+    } else if (base >= kMfmaTargetWG) {
+      plan->kgroups = 1;
+    } else {
+      const long long s2 = std::min(cdiv(kMfmaTargetWG / 2, base), std::max(n_tiles / 4, 1LL));
+      const bool short_groups = n_tiles / (2 * s2) < 8;
+      plan->kgroups = short_groups ? 1 : 2;
+      if (short_groups) target = kMfmaTargetWG / 2;
+    }
     if (opts && opts->kv_splits > 0) {
       splits = opts->kv_splits < n_tiles ? opts->kv_splits : n_tiles;
     } else {

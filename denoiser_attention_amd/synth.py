@@ -114,6 +114,12 @@ CONFIGS: dict[str, Config] = {c.name: c for c in [
     Config("decode_l1", 7, batch=8, prefix_len=2048, block_len=1, n_q_heads=32, n_kv_heads=2,
            head_dim=128, dtype="bf16", qkv_std=1.0, vocab=131072, logit_std=3.0, k=1, steps=1,
            description="supplementary: decode geometry at L1 (single-token decode attention)"),
+    # A prefix-bound shape large enough to be bandwidth-dominated: the high-batch
+    # geometry at a single-token block (268 MB of cache K/V per call).
+    Config("decode_b64_p4096_l1", 8, batch=64, prefix_len=4096, block_len=1, n_q_heads=32,
+           n_kv_heads=2, head_dim=128, dtype="bf16", qkv_std=1.0, vocab=131072, logit_std=3.0,
+           k=1, steps=1,
+           description="supplementary: high-batch geometry at L1 (prefix-bound, 268 MB of K/V)"),
 ]}
 
 # Prefix lengths of the 8K-generation workload: an isolated sweep, and the

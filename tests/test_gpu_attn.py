@@ -237,6 +237,7 @@ FULL = [
     ("highbatch_b64_p4096_l64", {}, [0, 63], [2, 29]),
     ("decode_l16", {}, [4], [0, 31]),
     ("decode_l1", {}, [0, 7], [3, 20]),
+    ("decode_b64_p4096_l1", {}, [0, 63], [1, 30]),
 ]
 
 
