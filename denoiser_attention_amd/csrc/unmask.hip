@@ -169,26 +169,48 @@ __global__ __launch_bounds__(kThreads) void topk_commit_kernel(UnmaskParams p) {
   if (tid < 2) s_count[tid] = 0;
   for (int l = L + tid; l < 16 * L16; l += kThreads) s_key[l] = 0;
 
-  // Merge: one thread per position combines the position's chunk triples in
-  // chunk order from a batch of independent 16-byte loads.  Every mask flag of
-  // the sequence is read before any is written, so mask_out may alias
-  // mask_state.
+  // Merge: one thread per position combines the position's chunk triples,
+  // 16 at a time: the batch maximum first, then the lowest id attaining it
+  // and the sum rescaled once to it (independent exponentials, a fixed
+  // order).  The first batch is loaded together with the mask flag (the
+  // workspace holds a slot for every position; an unmasked position's slot is
+  // loaded and ignored).  Every mask flag of the sequence is read before any
+  // is written, so mask_out may alias mask_state.
   constexpr int kMergeBatch = 16;
   int my_masked = 0, my_above = 0;
   for (int l = tid; l < L; l += kThreads) {
     uint64_t key = 0;
     int pred = -1;
+    const VocabPartial* pp = p.partials + (row0 + l) * (size_t)p.n_chunks;
+    VocabPartial q[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i)
+      if (i < p.n_chunks) q[i] = pp[i];
     if (p.mask_state[row0 + l] != 0) {
-      const VocabPartial* pp = p.partials + (row0 + l) * (size_t)p.n_chunks;
       Triple t{-INFINITY, INT_MAX, 0.0f};
       for (int c0 = 0; c0 < p.n_chunks; c0 += kMergeBatch) {
-        VocabPartial q[kMergeBatch];
+        if (c0 > 0) {
+#pragma unroll
+          for (int i = 0; i < kMergeBatch; ++i)
+            if (c0 + i < p.n_chunks) q[i] = pp[c0 + i];
+        }
+        const int nb = min(kMergeBatch, p.n_chunks - c0);
+        float bm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < kMergeBatch; ++i)
-          if (c0 + i < p.n_chunks) q[i] = pp[c0 + i];
+          if (i < nb) bm = fmaxf(bm, q[i].m);
+        int barg = INT_MAX;
+        float bs = 0.0f;
+        if (bm != -INFINITY) {
 #pragma unroll
-        for (int i = 0; i < kMergeBatch; ++i)
-          if (c0 + i < p.n_chunks) t = combine(t, Triple{q[i].m, q[i].arg, q[i].s});
+          for (int i = 0; i < kMergeBatch; ++i) {
+            if (i < nb && q[i].m != -INFINITY) {
+              bs += q[i].s * __builtin_amdgcn_exp2f((q[i].m - bm) * kLog2e);
+              if (q[i].m == bm) barg = min(barg, q[i].arg);
+            }
+          }
+        }
+        t = combine(t, Triple{bm, barg, bs});
       }
       const float conf = 1.0f / t.s;
       key = ((uint64_t)__float_as_uint(conf) << 32) | (uint64_t)(0xffffffffu - (uint32_t)l);
