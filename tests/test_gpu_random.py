@@ -89,3 +89,77 @@ def test_random_unmask(case):
     got = gpu_step(x, mask, tokens0, mode, split=split, **params)
     ref = oracle.unmask_step_select(x.astype(np.float64), mask, MODES[mode], **params)
     check_select(got, ref, mask, tokens0, mode, f"random {case[:6]}")
+
+
+def varlen_cases(n=16, seed=4048):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([2, 4, 16]))
+        cases.append((i, int(rng.integers(2, 6)), G * Hkv, Hkv, int(rng.integers(1, 41)),
+                      int(rng.integers(1, 400)), int(rng.choice([64, 128])),
+                      str(rng.choice(["auto", "mfma", "shuffle"])), int(rng.choice([0, 1, 3]))))
+    return cases
+
+
+@pytest.mark.parametrize("case", varlen_cases(), ids=lambda c: f"varlen{c[0]}")
+def test_random_varlen(case):
+    from test_gpu_varlen import gpu_varlen, oracle_varlen
+    i, B, Hq, Hkv, L, Pmax, D, path, splits = case
+    cfg = synth.get_config("decode_b8_p2048_l32").with_(batch=B, n_q_heads=Hq, n_kv_heads=Hkv,
+                                                        head_dim=D, block_len=L)
+    inp = synth.varlen_inputs(cfg, seed=200 + i, max_prefix_len=Pmax, prefix_cap=Pmax + i % 5)
+    got = gpu_varlen(inp, path=path, kv_splits=splits, out_dtype=torch.float32)
+    check_attn(got, oracle_varlen(inp), "bf16", False, f"random varlen {case}")
+
+
+def multiblock_cases(n=12, seed=5050):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([2, 4, 16]))
+        cases.append((i, int(rng.integers(1, 3)), G * Hkv, Hkv, int(rng.integers(1, 7)),
+                      int(rng.integers(1, 50)), int(rng.choice([64, 128])),
+                      str(rng.choice(["auto", "mfma", "shuffle"])), int(rng.choice([0, 2]))))
+    return cases
+
+
+@pytest.mark.parametrize("case", multiblock_cases(), ids=lambda c: f"multiblock{c[0]}")
+def test_random_multiblock(case):
+    from test_gpu_varlen import gpu_multiblock, oracle_multiblock
+    i, B, Hq, Hkv, N, S, D, path, splits = case
+    cfg = synth.get_config("decode_b8_p2048_l32").with_(batch=B, n_q_heads=Hq, n_kv_heads=Hkv,
+                                                        head_dim=D)
+    inp = synth.multiblock_inputs(cfg, N, S, seed=300 + i)
+    got = gpu_multiblock(inp, path=path, kv_splits=splits, out_dtype=torch.float32)
+    check_attn(got, oracle_multiblock(inp), "bf16", False, f"random multiblock {case}")
+
+
+def lmhead_cases(n=10, seed=6060):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        mode = str(rng.choice(list(MODES)))
+        if mode in ("top_k", "leftmost"):
+            params = dict(k=int(rng.integers(0, 9)))
+        elif mode == "threshold":
+            params = dict(gamma=float(rng.choice([0.5, 0.9])), steps_left=int(rng.integers(1, 5)))
+        else:
+            params = dict(step=1, n_steps=int(rng.integers(1, 5)))
+        cases.append((i, int(rng.integers(1, 5)), int(rng.integers(1, 60)),
+                      int(rng.integers(1, 3000)), int(32 * rng.integers(1, 9)),
+                      float(rng.uniform(0.2, 1.0)), mode, params))
+    return cases
+
+
+@pytest.mark.parametrize("case", lmhead_cases(), ids=lambda c: f"lmhead{c[0]}")
+def test_random_lmhead(case):
+    from test_gpu_lmhead import check
+    i, B, L, V, d, density, mode, params = case
+    cfg = synth.get_config("decode_b8_p2048_l32").with_(vocab=V)
+    inp = synth.lmhead_inputs(cfg, d_model=d, seed=400 + i, batch=B, block_len=L)
+    rng = np.random.default_rng(700 + i)
+    mask = (rng.random((B, L)) < density).astype(np.uint8)
+    check(inp, mask, mode, f"random lmhead {case[:6]}", **params)
