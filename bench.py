@@ -44,7 +44,9 @@ def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    # The GPU's clocks ramp up over the first ~20 ms of load after an idle
+    # spell (input setup): 2000 warm-up steps (~0.1 s) time the steady state.
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--prefix-len", type=int, default=None)
     ap.add_argument("--rotate", type=int, default=0, help="input sets rotated (0 = auto)")
@@ -158,12 +160,18 @@ def suite(args):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     def time_calls(fns, n=reps):
-        """Average us per call over back-to-back calls (rotating fns), HIP events."""
+        """Average us per call over back-to-back calls (rotating fns), HIP events,
+        after at least 50 ms of untimed calls (the clocks ramp up under load)."""
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
-            for i in range(3):
-                fns[i % len(fns)]()
+            t0 = time.perf_counter()
+            i = 0
+            while time.perf_counter() - t0 < 0.05:
+                for _ in range(8):
+                    fns[i % len(fns)]()
+                    i += 1
+                torch.cuda.synchronize()
             e0.record(stream)
             for i in range(n):
                 fns[i % len(fns)]()
