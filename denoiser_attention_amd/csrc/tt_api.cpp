@@ -123,7 +123,7 @@ tt_status plan_attn(long long B, int P, int L, int Hq, int Hkv, int D, tt_dtype 
     plan->stream_waves = sw8 ? 8 : 4;
     const long long base = (rows64 || sw8) ? base64 : base128;
     // With few query tiles, two wave groups per workgroup split each key range
-    // on chip -- unless that leaves each group fewer than 8 tiles, where the
+    // on chip -- unless that leaves each group 8 tiles or fewer, where the
     // pipeline start and the on-chip merge dominate: one group per workgroup
     // and about one workgroup per CU of key splits measured faster there.
     long long target = kMfmaTargetWG;
@@ -136,7 +136,7 @@ tt_status plan_attn(long long B, int P, int L, int Hq, int Hkv, int D, tt_dtype 
       plan->kgroups = 1;
     } else {
       const long long s2 = std::min(cdiv(kMfmaTargetWG / 2, base), std::max(n_tiles / 4, 1LL));
-      const bool short_groups = n_tiles / (2 * s2) < 8;
+      const bool short_groups = n_tiles / (2 * s2) <= 8;
       plan->kgroups = short_groups ? 1 : 2;
       if (short_groups) target = kMfmaTargetWG / 2;
     }
