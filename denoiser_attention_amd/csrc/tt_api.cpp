@@ -134,6 +134,13 @@ tt_status plan_attn(long long B, int P, int L, int Hq, int Hkv, int D, tt_dtype 
       plan->kgroups = req_groups;
     } else if (base >= kMfmaTargetWG) {
       plan->kgroups = 1;
+    } else if (M < tt::kAttnMfmaBM) {
+      // Fewer packed rows than one query tile (single-token and very short
+      // blocks): the matrix work is light and the call is a stream of K/V.
+      // One 4-wave workgroup per CU streaming a longer key range moved the
+      // bytes faster than two groups per workgroup or two workgroups per CU.
+      plan->kgroups = 1;
+      target = kMfmaTargetWG / 2;
     } else {
       const long long s2 = std::min(cdiv(kMfmaTargetWG / 2, base), std::max(n_tiles / 4, 1LL));
       const bool short_groups = n_tiles / (2 * s2) <= 8;
