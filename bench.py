@@ -9,6 +9,8 @@ timing starts; several independent input sets are rotated so that the working
 set exceeds the 256 MB Infinity Cache and every step streams from HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--graph]
+    python bench.py --suite                      (supplementary workloads)
+    python bench.py --attn-only --config NAME    (one attention workload, for counter runs)
 
 The timed loop issues each step's three library calls on one stream.  With
 --graph each input set's step is captured once into a HIP graph and the loop
@@ -57,6 +59,9 @@ def parse_args():
                     help="instead of the step: one JSON line per supplementary workload "
                          "(attention of every configuration, per-sequence prefixes, the "
                          "multi-block pass, selection rules, the fused LM head)")
+    ap.add_argument("--attn-only", action="store_true",
+                    help="instead of the step: only the attention call of --config "
+                         "(and --prefix-len), timed as the suite times it (for counter runs)")
     ap.add_argument("--kernel-reps", type=int, default=200,
                     help="back-to-back launches timed for the per-kernel roofline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -212,6 +217,12 @@ def suite(args):
              input_sets=n_sets)
         del keep, fns
 
+    if args.attn_only:
+        kw = {} if args.prefix_len is None else {"prefix_len": args.prefix_len}
+        cfg = synth.get_config(args.config, **kw)
+        attn_case(f"attn {args.config} P={cfg.prefix_len}", cfg)
+        return
+
     # Attention at every configuration (bf16) and the prefix-bound shapes.
     for name, kw in (("decode_b8_p2048_l32", {}), ("block256_b16_p1024", {}),
                      ("gen8k_b4_l256", dict(prefix_len=512)), ("gen8k_b4_l256", dict(prefix_len=8192)),
@@ -315,7 +326,7 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    if args.suite:
+    if args.suite or args.attn_only:
         suite(args)
         return
 
