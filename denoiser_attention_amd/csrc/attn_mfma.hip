@@ -106,6 +106,15 @@ __device__ __forceinline__ void dma16_s(const char* base, uint32_t off, uint32_t
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
+// Both forms with the non-temporal hint, for K/V tiles that few workgroups
+// read (a stream rather than a shared working set).
+__device__ __forceinline__ void dma16_nt(const char* g, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma16_s_nt(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+
 // Maximum of x over lanes l and l ^ 32, for every lane l.  v_permlane32_swap
 // exchanges the two 32-lane halves between its two results, so together they
 // hold both halves' values for each lane.
@@ -147,7 +156,10 @@ __device__ __forceinline__ void wait_tiles(int n_after) {
 // each K/V tile fetched into LDS feeds twice the matrix work: half the
 // global-to-LDS traffic, load instructions and LDS writes per unit of work.
 // One such workgroup per CU (two waves per SIMD).
-template <int D, int NS, int KG, int RB, int RG, bool OUT_BF16, bool POS_SCALE>
+// NT_LOADS: the K/V tile loads carry the non-temporal hint.  The launch plan
+// sets it when at most 4 query-tile workgroups read each tile, where the tiles
+// are a stream rather than a working set shared through L2.
+template <int D, int NS, int KG, int RB, int RG, bool OUT_BF16, bool POS_SCALE, bool NT_LOADS>
 __global__ __launch_bounds__(kThreads * KG * RG, RB == 2 ? 1 : 2 / (KG * RG))
 void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   using L = Lay<D>;
@@ -264,8 +276,13 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     for (int i = 0; i < LOADS; ++i) {
       const uint32_t wofs = (i * NT + wave * 64) * 16;   // wave-uniform destination
       if (uniform) {
-        dma16_s(kbase, koff[i], kst + wofs);
-        dma16_s(vbase, voff[i], vst + wofs);
+        if constexpr (NT_LOADS) {
+          dma16_s_nt(kbase, koff[i], kst + wofs);
+          dma16_s_nt(vbase, voff[i], vst + wofs);
+        } else {
+          dma16_s(kbase, koff[i], kst + wofs);
+          dma16_s(vbase, voff[i], vst + wofs);
+        }
       } else {
         const int j = min(key0 + rrow[i], n_keys - 1);
         const size_t rel = (size_t)rrow[i] * L::ROWB;
@@ -657,24 +674,35 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   const int m_tiles = (p.M + rows_wg - 1) / rows_wg;
   const long long n = (long long)m_tiles * p.splits * p.B * p.NB * p.Hkv;
   if (n <= 0 || n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // The non-temporal form is built for the 4-wave plans with a non-negative
+  // scale (where the streaming shapes run); elsewhere the hint is dropped.
+  const bool nt = POS && p.nt_loads != 0;
   if (p.rows_per_wave == 64 || p.stream_waves == 8) {
     if constexpr (D == 128) {
       if (p.kgroups != 1 || (p.rows_per_wave == 64 && p.stream_waves == 8)) return hipErrorInvalidValue;
       if (p.rows_per_wave == 64)
-        hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, 2, 1, OUT_BF16, POS>), dim3((unsigned)n),
-                           dim3(kThreads), 0, stream, p, m_tiles, (int)n);
+        hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, 2, 1, OUT_BF16, POS, false>),
+                           dim3((unsigned)n), dim3(kThreads), 0, stream, p, m_tiles, (int)n);
       else
-        hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, 1, 2, OUT_BF16, POS>), dim3((unsigned)n),
-                           dim3(2 * kThreads), 0, stream, p, m_tiles, (int)n);
+        hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, 1, 2, OUT_BF16, POS, false>),
+                           dim3((unsigned)n), dim3(2 * kThreads), 0, stream, p, m_tiles, (int)n);
     } else {
       return hipErrorInvalidValue;
     }
   } else if (p.kgroups == 2) {
-    hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 2, 1, 1, OUT_BF16, POS>), dim3((unsigned)n),
-                       dim3(2 * kThreads), 0, stream, p, m_tiles, (int)n);
+    if (nt)
+      hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 2, 1, 1, OUT_BF16, POS, POS>),
+                         dim3((unsigned)n), dim3(2 * kThreads), 0, stream, p, m_tiles, (int)n);
+    else
+      hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 2, 1, 1, OUT_BF16, POS, false>),
+                         dim3((unsigned)n), dim3(2 * kThreads), 0, stream, p, m_tiles, (int)n);
   } else {
-    hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, 1, 1, OUT_BF16, POS>), dim3((unsigned)n),
-                       dim3(kThreads), 0, stream, p, m_tiles, (int)n);
+    if (nt)
+      hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, 1, 1, OUT_BF16, POS, POS>),
+                         dim3((unsigned)n), dim3(kThreads), 0, stream, p, m_tiles, (int)n);
+    else
+      hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, 1, 1, 1, OUT_BF16, POS, false>),
+                         dim3((unsigned)n), dim3(kThreads), 0, stream, p, m_tiles, (int)n);
   }
   return hipGetLastError();
 }

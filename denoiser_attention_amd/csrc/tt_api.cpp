@@ -43,6 +43,7 @@ struct AttnPlan {
   int kgroups = 1;             // MFMA: wave groups splitting a workgroup's keys
   int rows_per_wave = 32;      // MFMA: query rows per wavefront
   int stream_waves = 4;        // MFMA: waves sharing one K/V tile stream
+  bool nt_loads = false;       // MFMA: non-temporal hint on the K/V tile loads
   int splits = 1;
   int tiles_per_split = 1;
   bool empty = false;          // nothing to compute
@@ -122,6 +123,11 @@ tt_status plan_attn(long long B, int P, int L, int Hq, int Hkv, int D, tt_dtype 
     const bool sw8 = req_sw == 8;
     plan->stream_waves = sw8 ? 8 : 4;
     const long long base = (rows64 || sw8) ? base64 : base128;
+    // When at most 4 query-tile workgroups read each K/V tile, the tiles are a
+    // stream and the non-temporal hint moves them faster (B64 P4096 L1: 55.8 ->
+    // 53.0 us; B8 P2048 L32: -2.5%); with 8 or more readers the hint costs L2
+    // reuse (B64 P4096 L64: +2%), and from 32 it is neutral.
+    plan->nt_loads = (rows64 || sw8 ? cdiv(M, 2 * tt::kAttnMfmaBM) : cdiv(M, tt::kAttnMfmaBM)) <= 4;
     // With few query tiles, two wave groups per workgroup split each key range
     // on chip -- unless that leaves each group 8 tiles or fewer, where the
     // pipeline start and the on-chip merge dominate: one group per workgroup
@@ -303,6 +309,7 @@ tt_status attn_run(const AttnCall& c) {
   p.kgroups = plan.kgroups;
   p.rows_per_wave = plan.rows_per_wave;
   p.stream_waves = plan.stream_waves;
+  p.nt_loads = plan.nt_loads ? 1 : 0;
   p.out_bf16 = c.out_dtype == TT_BF16 ? 1 : 0;
   p.scale_log2 = c.scale * kLog2e;
   if (plan.splits > 1) {

@@ -45,6 +45,8 @@ struct AttnParams {
   int rows_per_wave;   // MFMA kernel: 32, or 64 (head_dim 128, one key group)
   int stream_waves;    // MFMA kernel: waves sharing one K/V stream, 4 or 8 (head_dim 128,
                        // one key group, 32-row waves)
+  int nt_loads;        // MFMA kernel: 1 = K/V tile loads carry the non-temporal hint
+                       // (each tile is read by few query-tile workgroups)
   int out_bf16;        // 1: write bf16 output, 0: fp32
   float scale_log2;    // softmax scale * log2(e)
 };
