@@ -251,3 +251,28 @@ def test_full_size_sampled(name, kw, batches, heads):
     for (b, h), o in ref.items():
         check_attn(got[b, h], o, "bf16", True, f"{name} b={b} h={h}")
     assert np.isfinite(got).all()
+
+
+def test_split_plans_reuse_one_workspace():
+    """One workspace, reused by consecutive calls of different shapes and
+    split counts (each shape twice), gives the oracle's output every time:
+    nothing a call leaves in the workspace may leak into the next."""
+    from denoiser_attention_amd import attn_workspace_bytes, block_attn
+    # (B, Hq, Hkv, L, P, D, kv_splits): M = G*L below 128 rows, several splits.
+    cases = [(8, 32, 2, 1, 700, 128, 0), (3, 16, 1, 4, 1000, 128, 5), (8, 32, 2, 1, 700, 128, 3),
+             (2, 8, 2, 9, 333, 64, 7), (4, 32, 2, 2, 2000, 128, 0)]
+    need = max(attn_workspace_bytes(B, P, L, Hq, Hkv, D, torch.bfloat16, "mfma", s)
+               for B, Hq, Hkv, L, P, D, s in cases)
+    assert need > 0
+    ws = torch.full((need,), 0x7f, dtype=torch.uint8, device=DEV)
+    for rep in range(2):
+        for i, (B, Hq, Hkv, L, P, D, s) in enumerate(cases):
+            cfg = small_cfg(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, prefix_len=P,
+                            block_len=L)
+            inp = synth.attn_inputs(cfg, seed=40 + i, prefix_cap=P + 5)
+            t = {n: to_dev(inp[n], DEV) for n in ("q", "k_ctx", "v_ctx", "k_blk", "v_blk")}
+            out = block_attn(t["q"], t["k_ctx"], t["v_ctx"], P, t["k_blk"], t["v_blk"], inp["scale"],
+                             path="mfma", kv_splits=s, workspace=ws)
+            torch.cuda.synchronize()
+            got = out.float().cpu().numpy().astype(np.float64)
+            check_attn(got, oracle_attn(inp), "bf16", True, f"rep {rep} case {i} {cases[i]}")
