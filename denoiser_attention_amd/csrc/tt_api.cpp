@@ -124,8 +124,8 @@ tt_status plan_attn(long long B, int P, int L, int Hq, int Hkv, int D, tt_dtype 
     plan->stream_waves = sw8 ? 8 : 4;
     const long long base = (rows64 || sw8) ? base64 : base128;
     // When at most 4 query-tile workgroups read each K/V tile, the tiles are a
-    // stream and the non-temporal hint moves them faster (B64 P4096 L1: 55.8 ->
-    // 53.0 us; B8 P2048 L32: -2.5%); with 8 or more readers the hint costs L2
+    // stream and the non-temporal hint moves them faster (B64 P4096 L1: 53.6 ->
+    // 50.5 us; B8 P2048 L32: -1.6%); with 8 or more readers the hint costs L2
     // reuse (B64 P4096 L64: +2%), and from 32 it is neutral.
     plan->nt_loads = (rows64 || sw8 ? cdiv(M, 2 * tt::kAttnMfmaBM) : cdiv(M, tt::kAttnMfmaBM)) <= 4;
     // With few query tiles, two wave groups per workgroup split each key range
