@@ -253,6 +253,30 @@ def test_full_size_sampled(name, kw, batches, heads):
     assert np.isfinite(got).all()
 
 
+# Sizes past the configurations: a 262K-key context (8193 key tiles, 268 MB of
+# cache K/V for one sequence), a 512-pair single-token batch, and a 64K-key
+# fp32 context on the shuffle kernel.
+LARGE = [
+    ("decode_b8_p2048_l32", dict(batch=1, prefix_len=262133, prefix_cap=262144, block_len=16),
+     [0], [0, 31], "bf16"),
+    ("decode_b8_p2048_l32", dict(batch=256, prefix_len=1000, block_len=1), [0, 255], [0, 31],
+     "bf16"),
+    ("tiny_fp32", dict(prefix_len=65531, prefix_cap=65536), [0], [0, 3], "fp32"),
+]
+
+
+@pytest.mark.parametrize("name,kw,batches,heads,dt", LARGE, ids=[f"{f[0]}-{f[1]}" for f in LARGE])
+def test_large_sizes_sampled(name, kw, batches, heads, dt):
+    cfg = synth.get_config(name)
+    say(f"large attention {name} {kw}")
+    inp = synth.attn_inputs(cfg, seed=5, step=0, **kw)
+    got = gpu_attn(inp, DEV)
+    ref = oracle_attn(inp, heads=heads, batches=batches)
+    for (b, h), o in ref.items():
+        check_attn(got[b, h], o, dt, dt == "bf16", f"{name} {kw} b={b} h={h}")
+    assert np.isfinite(got).all()
+
+
 def test_split_plans_reuse_one_workspace():
     """One workspace, reused by consecutive calls of different shapes and
     split counts (each shape twice), gives the oracle's output every time:
