@@ -114,6 +114,22 @@ def test_vocab_sizes_and_tails(V):
     _single(x, mask, 3)
 
 
+@pytest.mark.parametrize("V", [(1 << 20) + 4100, (1 << 20) + 4099])
+def test_large_vocab(V):
+    """A vocabulary past 2^20 (129 chunks, a ragged last chunk; 16-byte rows
+    and, with V odd, the scalar-load form), with the argmax planted in the last
+    chunk for one row and duplicated across the first and last chunk for
+    another (lowest id wins)."""
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((1, 4, V)) * 3).astype(np.float32)
+    x[0, 1, V - 2] = 40.0
+    x[0, 2, 17] = 40.0
+    x[0, 2, V - 1] = 40.0
+    mask = np.ones((1, 4), np.uint8)
+    got, _ = _single(x, mask, 2)
+    assert got["pred"][0, 1] == V - 2 and got["pred"][0, 2] == 17
+
+
 def test_k_edge_cases():
     rng = np.random.default_rng(7)
     x = (rng.standard_normal((3, 12, 5000)) * 2).astype(np.float32)
