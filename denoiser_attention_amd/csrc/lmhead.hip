@@ -61,9 +61,12 @@ static_assert(kLmVocab == 64 * 4, "four 64-entry vocabulary ranges per workgroup
 static_assert(kLmRows == 256 && kLmK == 32, "tile shape");
 static_assert(NS * STAGE <= 160 * 1024, "ring fits the LDS");
 
-// Chunk q (16 bytes) of stage row r lives in slot q ^ f(r): eight consecutive
-// rows read at the same chunk then hit eight distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+// Chunk q (16 bytes) of stage row r lives in slot q ^ f(r).  A 16-byte LDS
+// read is served 16 lanes (256 bytes) at a time; those lanes read 16
+// consecutive 64-byte rows at the same chunk, which f spreads over all 16
+// 16-byte bank groups (rows r and r + 4 differ in f, rows r .. r + 3 in their
+// 64-byte base).  Measured: no LDS bank conflicts.
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
 struct Triple {
   float m;
