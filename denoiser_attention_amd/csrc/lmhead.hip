@@ -24,13 +24,15 @@
 //                           waves of its row half through LDS.  Wave w covers
 //                           vocabulary entries 64(w%4)..+63 of the slice
 //                           against rows 128(w/4)..+127 (8 accumulator
-//                           tiles).  W and H tiles of 32 d_model columns
-//                           stream into a 4-stage LDS ring (128 KB, one
-//                           workgroup per CU) with 16-byte direct-to-LDS
-//                           loads (rows XOR-swizzled at 16-byte granularity);
-//                           3 stages are in flight while one is consumed, so
-//                           the weight stream from HBM has about 1.5 us of
-//                           lead, and each weight tile feeds 256 rows.
+//                           tiles).  W and H tiles of 64 d_model columns
+//                           (whole 128-byte weight lines) stream into a
+//                           2-stage LDS ring (128 KB, one workgroup per CU)
+//                           with 16-byte direct-to-LDS loads (rows
+//                           XOR-swizzled at 16-byte granularity): one stage
+//                           loads while the other is consumed, one barrier
+//                           per 64 columns, and each weight tile feeds 256
+//                           rows.  A d_model that is an odd multiple of 32
+//                           ends with a 32-column stage.
 //   lmhead_merge_kernel  -- one wavefront per masked row: merges the row's
 //                           slice partials into one.
 // The confidence-ranking and commit step then runs on the merged partials.
@@ -49,24 +51,24 @@ typedef __attribute__((address_space(3))) char lds_char;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 8;                          // 4 vocabulary ranges x 2 row halves
 constexpr int kThreads = 64 * kWaves;
-constexpr int NS = 4;                               // ring stages (one workgroup per CU)
-constexpr int ROWB = kLmK * 2;                      // bytes of one row of a stage (64)
+constexpr int NS = 2;                               // ring stages (one workgroup per CU)
+constexpr int KS = 64;                              // d_model columns per stage
+constexpr int ROWB = KS * 2;                        // bytes of one row of a stage (128)
 constexpr int W_TILE = kLmVocab * ROWB;             // 16 KB
 constexpr int H_TILE = kLmRows * ROWB;              // 16 KB
 constexpr int STAGE = W_TILE + H_TILE;              // 32 KB
 constexpr int W_LOADS = W_TILE / 16 / kThreads;     // 2 direct loads per thread
 constexpr int H_LOADS = H_TILE / 16 / kThreads;     // 2
-constexpr int PER_STAGE = W_LOADS + H_LOADS;        // vector-memory ops per stage
 static_assert(kLmVocab == 64 * 4, "four 64-entry vocabulary ranges per workgroup");
-static_assert(kLmRows == 256 && kLmK == 32, "tile shape");
+static_assert(kLmRows == 256 && KS == 64, "tile shape");
 static_assert(NS * STAGE <= 160 * 1024, "ring fits the LDS");
 
 // Chunk q (16 bytes) of stage row r lives in slot q ^ f(r).  A 16-byte LDS
 // read is served 16 lanes (256 bytes) at a time; those lanes read 16
-// consecutive 64-byte rows at the same chunk, which f spreads over all 16
-// 16-byte bank groups (rows r and r + 4 differ in f, rows r .. r + 3 in their
-// 64-byte base).  Measured: no LDS bank conflicts.
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// consecutive 128-byte rows at the same chunk, which f spreads over all 16
+// 16-byte bank groups (rows r and r + 1 differ in their 128-byte base, pairs
+// of rows in f).
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 struct Triple {
   float m;
@@ -103,17 +105,6 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 __device__ __forceinline__ void dma16_s(const char* base, uint32_t off, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
-
-__device__ __forceinline__ void wait_stages(int n_after) {
-  switch (n_after) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<PER_STAGE>(); break;
-    case 2: wait_vmcnt<2 * PER_STAGE>(); break;
-    case 3: wait_vmcnt<3 * PER_STAGE>(); break;
-    default: wait_vmcnt<4 * PER_STAGE>(); break;
-  }
-}
-static_assert(NS - 2 <= 4, "waits above cover NS - 2 stages in flight");
 
 __global__ __launch_bounds__(1024) void lmhead_rows_kernel(LmParams p) {
   __shared__ int s_wave[16];
@@ -160,31 +151,40 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_stats_kernel(LmParams p, i
 
   // Per-thread direct-load offsets (bytes from the stage's column base).
   uint32_t woff[W_LOADS], hoff[H_LOADS];
+  bool wlo[W_LOADS], hlo[H_LOADS];   // the load's global chunk lies in the first 32 columns
 #pragma unroll
   for (int j = 0; j < W_LOADS; ++j) {
-    const int i = tid + kThreads * j, r = i >> 2, q = i & 3;
+    const int i = tid + kThreads * j, r = i >> 3, q = i & 7;
     const int v = min(vocab0 + r, p.V - 1);        // past the vocabulary: a valid row, masked later
     woff[j] = (uint32_t)((size_t)(v - vocab0) * rowb) + ((q ^ swz(r)) << 4);
+    wlo[j] = (q ^ swz(r)) < 4;
   }
 #pragma unroll
   for (int j = 0; j < H_LOADS; ++j) {
-    const int i = tid + kThreads * j, r = i >> 2, q = i & 3;
+    const int i = tid + kThreads * j, r = i >> 3, q = i & 7;
     const int row = p.row_ids[row0 + min(r, rows_here - 1)];
     hoff[j] = (uint32_t)((size_t)row * rowb) + ((q ^ swz(r)) << 4);
+    hlo[j] = (q ^ swz(r)) < 4;
   }
   const char* wbase = static_cast<const char*>(p.weight) + (size_t)vocab0 * rowb;
   const char* hbase = static_cast<const char*>(p.hidden);
   const uint32_t ring_u32 = (uint32_t)(uintptr_t)(lds_char*)ring;
 
+  // Column tile kt; the last tile of a d_model that is an odd multiple of 32
+  // holds 32 columns, and only the loads of those columns are issued.
+  const int nfull = d / KS;
+  const int ntile = nfull + (d % KS != 0 ? 1 : 0);
   auto issue = [&](int kt, int slot) {
     const uint32_t st = ring_u32 + slot * STAGE;
     const char* wk = wbase + (size_t)kt * ROWB;
     const char* hk = hbase + (size_t)kt * ROWB;
+    const bool half = kt >= nfull;
 #pragma unroll
-    for (int j = 0; j < W_LOADS; ++j) dma16_s(wk, woff[j], st + (kThreads * j + wave * 64) * 16);
+    for (int j = 0; j < W_LOADS; ++j)
+      if (!half || wlo[j]) dma16_s(wk, woff[j], st + (kThreads * j + wave * 64) * 16);
 #pragma unroll
     for (int j = 0; j < H_LOADS; ++j)
-      dma16_s(hk, hoff[j], st + W_TILE + (kThreads * j + wave * 64) * 16);
+      if (!half || hlo[j]) dma16_s(hk, hoff[j], st + W_TILE + (kThreads * j + wave * 64) * 16);
   };
 
   // Operand rows of this lane: vocabulary rows 64*vw + 32*vt + (lane & 31),
@@ -203,65 +203,52 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_stats_kernel(LmParams p, i
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[vt][t] = f32x16{};
 
-  auto compute = [&](auto slot_c) {
+  auto compute = [&](auto slot_c, int n_halves) {
     const int slot = slot_c;
     const char* st = ring + slot * STAGE;
-    bf16x8 a[kLmK / 16][2], bq[kLmK / 16][4];
 #pragma unroll
-    for (int s = 0; s < kLmK / 16; ++s) {
-      const int c = 2 * s + hh;
+    for (int half = 0; half < KS / 32; ++half) {
+      if (half >= n_halves) break;
+      bf16x8 a[2][2], bq[2][4];
 #pragma unroll
-      for (int vt = 0; vt < 2; ++vt)
-        a[s][vt] = *reinterpret_cast<const bf16x8*>(st + a_row[vt] * ROWB + ((c ^ swz(a_row[vt])) << 4));
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int c = 2 * (2 * half + s2) + hh;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        bq[s][t] = *reinterpret_cast<const bf16x8*>(st + W_TILE + b_row[t] * ROWB +
-                                                    ((c ^ swz(b_row[t])) << 4));
-    }
-#pragma unroll
-    for (int s = 0; s < kLmK / 16; ++s)
-#pragma unroll
-      for (int vt = 0; vt < 2; ++vt)
+        for (int vt = 0; vt < 2; ++vt)
+          a[s2][vt] = *reinterpret_cast<const bf16x8*>(st + a_row[vt] * ROWB + ((c ^ swz(a_row[vt])) << 4));
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          acc[vt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s][vt], bq[s][t], acc[vt][t], 0, 0, 0);
+          bq[s2][t] = *reinterpret_cast<const bf16x8*>(st + W_TILE + b_row[t] * ROWB +
+                                                       ((c ^ swz(b_row[t])) << 4));
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            acc[vt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s2][vt], bq[s2][t], acc[vt][t], 0, 0, 0);
+    }
   };
 
-  // Ring: stage i is refilled with column tile i + NS - 1 right after the
-  // barrier of iteration i + 1, when every wave has finished with it.
-  const int nk = d / kLmK;
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s, s);
+  // Two stages: the next column tile loads while this one is consumed.
+  issue(0, 0);
   int i = 0;
-  // Steady state, unrolled by the ring depth: each stage's slot is a
-  // compile-time constant (its offsets fold into the LDS reads), the wait is a
-  // constant count, and every fragment of a stage is read before its MFMAs
-  // (6-7% faster than the rolled loop); the last stages take the general form.
-  static_assert(NS == 4, "the unrolled steady state assumes a 4-stage ring");
-  for (; i + NS - 1 + 3 < nk; i += 4) {
-    wait_vmcnt<(NS - 2) * PER_STAGE>();
+  for (; i + 2 < nfull; i += 2) {
+    wait_vmcnt<0>();
     barrier();
-    issue(i + NS - 1, (NS - 1) % NS);
-    compute(std::integral_constant<int, 0>{});
-    wait_vmcnt<(NS - 2) * PER_STAGE>();
+    issue(i + 1, 1);
+    compute(std::integral_constant<int, 0>{}, 2);
+    wait_vmcnt<0>();
     barrier();
-    issue(i + NS, 0);
-    compute(std::integral_constant<int, 1>{});
-    wait_vmcnt<(NS - 2) * PER_STAGE>();
-    barrier();
-    issue(i + NS + 1, 1);
-    compute(std::integral_constant<int, 2>{});
-    wait_vmcnt<(NS - 2) * PER_STAGE>();
-    barrier();
-    issue(i + NS + 2, 2);
-    compute(std::integral_constant<int, 3>{});
+    issue(i + 2, 0);
+    compute(std::integral_constant<int, 1>{}, 2);
   }
-  for (; i < nk; ++i) {
-    wait_stages(min(NS - 2, nk - 1 - i));
+  for (; i < ntile; ++i) {
+    wait_vmcnt<0>();
     barrier();
-    if (i + NS - 1 < nk) issue(i + NS - 1, (i + NS - 1) % NS);
-    compute(i % NS);
+    if (i + 1 < ntile) issue(i + 1, (i + 1) % NS);
+    compute(i % NS, i < nfull ? 2 : 1);
   }
 
   // Statistics of each hidden row over this wave's 64 entries.  Accumulator

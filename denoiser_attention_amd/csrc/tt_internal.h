@@ -152,7 +152,7 @@ hipError_t launch_topk_commit(const UnmaskParams& p, hipStream_t stream);
 // Fused LM-head projection + vocabulary statistics.
 constexpr int kLmRows = 256;     // hidden rows per workgroup
 constexpr int kLmVocab = 256;    // vocabulary entries per workgroup (one slice)
-constexpr int kLmK = 32;         // d_model per pipeline stage
+constexpr int kLmK = 32;         // d_model granularity (stages take 64 columns, the last may take 32)
 struct LmParams {
   const void* hidden;        // [B*L, d] bf16
   const void* weight;        // [V, d] bf16
