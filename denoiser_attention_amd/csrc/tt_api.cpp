@@ -197,6 +197,7 @@ tt_status to_status(hipError_t e) { return e == hipSuccess ? TT_OK : TT_EHIP; }
 
 struct UnmaskPlan {
   int n_chunks = 0;
+  int chunk = 0;
   size_t ws_bytes = 0;
   bool empty = false;
 };
@@ -204,7 +205,11 @@ struct UnmaskPlan {
 tt_status plan_unmask(int B, int L, int V, UnmaskPlan* plan) {
   if (B < 0 || L < 0 || V < 1) return TT_EINVAL;
   if (L > tt::kUnmaskMaxL) return TT_EUNSUPPORTED;
-  plan->n_chunks = (int)cdiv(V, tt::kVocabChunk);
+  // With many positions per call the grid is large either way, and 16 KB
+  // chunks stream faster (4096 rows: step 2.5% faster); with few, the commit's
+  // second round of chunk loads would cost more than the pass gains.
+  plan->chunk = (long long)B * L >= tt::kVocabChunkRows ? tt::kVocabChunkManyRows : tt::kVocabChunk;
+  plan->n_chunks = (int)cdiv(V, plan->chunk);
   plan->empty = (B == 0 || L == 0);
   const long long wgs = (long long)B * L * plan->n_chunks;
   if (wgs > INT_MAX) return TT_EUNSUPPORTED;
@@ -423,6 +428,7 @@ tt_status unmask_prepare(const float* logits, const uint8_t* mask_state, int bat
   p->L = block_len;
   p->V = vocab;
   p->n_chunks = plan->n_chunks;
+  p->chunk = plan->chunk;
   return TT_OK;
 }
 

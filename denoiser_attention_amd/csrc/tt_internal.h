@@ -128,6 +128,8 @@ struct VocabPartial {
 };
 
 constexpr int kVocabChunk = 8192;    // logits per chunk (32 KB)
+constexpr int kVocabChunkManyRows = 4096;   // logits per chunk from kVocabChunkRows rows on
+constexpr int kVocabChunkRows = 1024;
 constexpr int kUnmaskMaxL = 1024;    // block_len limit of the commit kernel
 
 struct UnmaskParams {
@@ -139,6 +141,7 @@ struct UnmaskParams {
   int32_t* pred_out;        // optional
   VocabPartial* partials;   // [B*L, n_chunks]
   int B, L, V, k, n_chunks;
+  int chunk;                // logits per chunk of the vocabulary pass
   // Selection rule (values of tt_select_mode) and its parameters.
   int mode;
   float gamma;

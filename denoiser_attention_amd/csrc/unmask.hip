@@ -7,9 +7,10 @@
 // of each sequence are committed (ties: lower position first), the rest stay
 // masked.  Logit rows of positions that are not masked are never read.
 //
-// vocab_reduce_kernel -- the HBM-bound pass.  A workgroup reduces one 8192-logit
-//   (32 KB) chunk of one masked row: every thread issues all of its 128-bit
-//   loads up front (8 x 16 B), takes the max / lowest-id argmax over its 32
+// vocab_reduce_kernel -- the HBM-bound pass.  A workgroup reduces one chunk
+//   of one masked row: 8192 logits (32 KB), or 4096 when a call covers at least
+//   1024 positions (the plan's choice).  Every thread issues all of its 128-bit
+//   loads up front (8 or 4 x 16 B), takes the max / lowest-id argmax over its
 //   values on the raw fp32 logits, then its sum of exp2((x - max) * log2 e);
 //   across the wave the maximum is found first (xor shuffles), then the lowest
 //   id attaining it and the sum rescaled once to it; the 4 waves' (max,
@@ -34,9 +35,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kVecPerThread = kVocabChunk / (kThreads * 4);      // 8 float4 loads
-constexpr int kScalarPerThread = kVocabChunk / kThreads;         // 32 scalar loads
-static_assert(kVocabChunk % (kThreads * 4) == 0, "chunk must be a multiple of 1024");
+static_assert(kVocabChunk % (kThreads * 4) == 0 && kVocabChunkManyRows % (kThreads * 4) == 0,
+              "chunks must be multiples of 1024 logits");
 
 struct Triple {
   float m;
@@ -56,8 +56,10 @@ __device__ __forceinline__ Triple combine(Triple a, Triple b) {
   return r;
 }
 
-template <bool VEC>
+template <bool VEC, int CHUNK>
 __global__ __launch_bounds__(kThreads) void vocab_reduce_kernel(UnmaskParams p) {
+  constexpr int kVecPerThread = CHUNK / (kThreads * 4);   // float4 loads per thread
+  constexpr int kScalarPerThread = CHUNK / kThreads;      // scalar loads per thread
   const size_t gid = blockIdx.x;
   const size_t row = gid / (size_t)p.n_chunks;
   const int chunk = (int)(gid % (size_t)p.n_chunks);
@@ -65,8 +67,8 @@ __global__ __launch_bounds__(kThreads) void vocab_reduce_kernel(UnmaskParams p) 
 
   const int tid = threadIdx.x;
   const int V = p.V;
-  const int c0 = chunk * kVocabChunk;
-  const int c1 = min(V, c0 + kVocabChunk);
+  const int c0 = chunk * CHUNK;
+  const int c1 = min(V, c0 + CHUNK);
   const float* x = p.logits + row * (size_t)V;
 
   Triple t{-INFINITY, INT_MAX, 0.0f};
@@ -286,12 +288,22 @@ hipError_t launch_vocab_reduce(const UnmaskParams& p, hipStream_t stream) {
   const long long n = (long long)p.B * p.L * p.n_chunks;
   if (n <= 0 || n > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const bool vec = (p.V % 4 == 0) && ((reinterpret_cast<uintptr_t>(p.logits) & 15) == 0);
-  if (vec) {
-    hipLaunchKernelGGL(vocab_reduce_kernel<true>, dim3((unsigned)n), dim3(kThreads), 0, stream,
-                       p);
+  if (p.chunk == kVocabChunk) {
+    if (vec)
+      hipLaunchKernelGGL((vocab_reduce_kernel<true, kVocabChunk>), dim3((unsigned)n), dim3(kThreads),
+                         0, stream, p);
+    else
+      hipLaunchKernelGGL((vocab_reduce_kernel<false, kVocabChunk>), dim3((unsigned)n),
+                         dim3(kThreads), 0, stream, p);
+  } else if (p.chunk == kVocabChunkManyRows) {
+    if (vec)
+      hipLaunchKernelGGL((vocab_reduce_kernel<true, kVocabChunkManyRows>), dim3((unsigned)n),
+                         dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((vocab_reduce_kernel<false, kVocabChunkManyRows>), dim3((unsigned)n),
+                         dim3(kThreads), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(vocab_reduce_kernel<false>, dim3((unsigned)n), dim3(kThreads), 0, stream,
-                       p);
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
