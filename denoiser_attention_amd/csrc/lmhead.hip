@@ -25,11 +25,12 @@
 //                           vocabulary entries 64(w%4)..+63 of the slice
 //                           against rows 128(w/4)..+127 (8 accumulator
 //                           tiles).  W and H tiles of 64 d_model columns
-//                           (whole 128-byte weight lines) stream into a
-//                           2-stage LDS ring (128 KB, one workgroup per CU)
-//                           with 16-byte direct-to-LDS loads (rows
-//                           XOR-swizzled at 16-byte granularity): one stage
-//                           loads while the other is consumed, one barrier
+//                           (whole 128-byte weight lines) stream with 16-byte
+//                           direct-to-LDS loads (rows XOR-swizzled at 16-byte
+//                           granularity) into a 3-stage weight ring and a
+//                           2-stage hidden ring (160 KB, one workgroup per
+//                           CU): the weight stream from HBM runs two tiles
+//                           ahead, the hidden rows (from L2) one; one barrier
 //                           per 64 columns, and each weight tile feeds 256
 //                           rows.  A d_model that is an odd multiple of 32
 //                           ends with a 32-column stage.
@@ -38,6 +39,7 @@
 // The confidence-ranking and commit step then runs on the merged partials.
 #include <climits>
 #include <type_traits>
+#include <utility>
 
 #include "tt_internal.h"
 
@@ -51,17 +53,18 @@ typedef __attribute__((address_space(3))) char lds_char;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 8;                          // 4 vocabulary ranges x 2 row halves
 constexpr int kThreads = 64 * kWaves;
-constexpr int NS = 2;                               // ring stages (one workgroup per CU)
+constexpr int NSW = 3;                              // weight ring stages
+constexpr int NSH = 2;                              // hidden ring stages
 constexpr int KS = 64;                              // d_model columns per stage
 constexpr int ROWB = KS * 2;                        // bytes of one row of a stage (128)
 constexpr int W_TILE = kLmVocab * ROWB;             // 16 KB
 constexpr int H_TILE = kLmRows * ROWB;              // 16 KB
-constexpr int STAGE = W_TILE + H_TILE;              // 32 KB
 constexpr int W_LOADS = W_TILE / 16 / kThreads;     // 2 direct loads per thread
 constexpr int H_LOADS = H_TILE / 16 / kThreads;     // 2
 static_assert(kLmVocab == 64 * 4, "four 64-entry vocabulary ranges per workgroup");
 static_assert(kLmRows == 256 && KS == 64, "tile shape");
-static_assert(NS * STAGE <= 160 * 1024, "ring fits the LDS");
+constexpr int RING = NSW * W_TILE + NSH * H_TILE;   // 160 KB: one workgroup per CU
+static_assert(RING <= 160 * 1024, "rings fit the LDS");
 
 // Chunk q (16 bytes) of stage row r lives in slot q ^ f(r).  A 16-byte LDS
 // read is served 16 lanes (256 bytes) at a time; those lanes read 16
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(1024) void lmhead_rows_kernel(LmParams p) {
 }
 
 __global__ __launch_bounds__(kThreads, 1) void lmhead_stats_kernel(LmParams p, int n_rt) {
-  __shared__ __attribute__((aligned(1024))) char ring[NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) char ring[RING];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -174,17 +177,23 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_stats_kernel(LmParams p, i
   // holds 32 columns, and only the loads of those columns are issued.
   const int nfull = d / KS;
   const int ntile = nfull + (d % KS != 0 ? 1 : 0);
-  auto issue = [&](int kt, int slot) {
-    const uint32_t st = ring_u32 + slot * STAGE;
+  // Weight tile kt goes to weight slot kt % 3, hidden tile kt to hidden slot
+  // kt % 2 (the hidden rows come from L2 and need less lead).
+  auto issue_w = [&](int kt, int wslot) {
+    const uint32_t st = ring_u32 + wslot * W_TILE;
     const char* wk = wbase + (size_t)kt * ROWB;
-    const char* hk = hbase + (size_t)kt * ROWB;
     const bool half = kt >= nfull;
 #pragma unroll
     for (int j = 0; j < W_LOADS; ++j)
       if (!half || wlo[j]) dma16_s(wk, woff[j], st + (kThreads * j + wave * 64) * 16);
+  };
+  auto issue_h = [&](int kt, int hslot) {
+    const uint32_t st = ring_u32 + NSW * W_TILE + hslot * H_TILE;
+    const char* hk = hbase + (size_t)kt * ROWB;
+    const bool half = kt >= nfull;
 #pragma unroll
     for (int j = 0; j < H_LOADS; ++j)
-      if (!half || hlo[j]) dma16_s(hk, hoff[j], st + W_TILE + (kThreads * j + wave * 64) * 16);
+      if (!half || hlo[j]) dma16_s(hk, hoff[j], st + (kThreads * j + wave * 64) * 16);
   };
 
   // Operand rows of this lane: vocabulary rows 64*vw + 32*vt + (lane & 31),
@@ -203,9 +212,10 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_stats_kernel(LmParams p, i
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[vt][t] = f32x16{};
 
-  auto compute = [&](auto slot_c, int n_halves) {
-    const int slot = slot_c;
-    const char* st = ring + slot * STAGE;
+  auto compute = [&](auto wslot_c, auto hslot_c, int n_halves) {
+    const int wslot = wslot_c, hslot = hslot_c;
+    const char* sw = ring + wslot * W_TILE;
+    const char* sh = ring + NSW * W_TILE + hslot * H_TILE;
 #pragma unroll
     for (int half = 0; half < KS / 32; ++half) {
       if (half >= n_halves) break;
@@ -215,10 +225,10 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_stats_kernel(LmParams p, i
         const int c = 2 * (2 * half + s2) + hh;
 #pragma unroll
         for (int vt = 0; vt < 2; ++vt)
-          a[s2][vt] = *reinterpret_cast<const bf16x8*>(st + a_row[vt] * ROWB + ((c ^ swz(a_row[vt])) << 4));
+          a[s2][vt] = *reinterpret_cast<const bf16x8*>(sw + a_row[vt] * ROWB + ((c ^ swz(a_row[vt])) << 4));
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          bq[s2][t] = *reinterpret_cast<const bf16x8*>(st + W_TILE + b_row[t] * ROWB +
+          bq[s2][t] = *reinterpret_cast<const bf16x8*>(sh + b_row[t] * ROWB +
                                                        ((c ^ swz(b_row[t])) << 4));
       }
 #pragma unroll
@@ -231,25 +241,31 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_stats_kernel(LmParams p, i
     }
   };
 
-  // Two stages: the next column tile loads while this one is consumed.
-  issue(0, 0);
+  // Issue order: W0 H0 W1, then after the barrier of step t: H(t+1) W(t+2).
+  // At step t the loads still allowed in flight are those of W(t+1) only, so
+  // the weight stream runs two tiles ahead and the hidden stream one.
+  issue_w(0, 0);
+  issue_h(0, 0);
+  if (ntile > 1) issue_w(1, 1);
+  using std::integral_constant;
+  auto step = [&](int t, auto ws, auto hs, int n_halves) {
+    if (t + 1 < ntile) wait_vmcnt<W_LOADS>(); else wait_vmcnt<0>();
+    barrier();
+    if (t + 1 < ntile) issue_h(t + 1, (t + 1) % NSH);
+    if (t + 2 < ntile) issue_w(t + 2, (t + 2) % NSW);
+    compute(ws, hs, n_halves);
+  };
   int i = 0;
-  for (; i + 2 < nfull; i += 2) {
-    wait_vmcnt<0>();
-    barrier();
-    issue(i + 1, 1);
-    compute(std::integral_constant<int, 0>{}, 2);
-    wait_vmcnt<0>();
-    barrier();
-    issue(i + 2, 0);
-    compute(std::integral_constant<int, 1>{}, 2);
+  // Steady state, unrolled by 6 (both rings' periods): constant slots.
+  for (; i + 6 < nfull; i += 6) {
+    step(i, integral_constant<int, 0>{}, integral_constant<int, 0>{}, 2);
+    step(i + 1, integral_constant<int, 1>{}, integral_constant<int, 1>{}, 2);
+    step(i + 2, integral_constant<int, 2>{}, integral_constant<int, 0>{}, 2);
+    step(i + 3, integral_constant<int, 0>{}, integral_constant<int, 1>{}, 2);
+    step(i + 4, integral_constant<int, 1>{}, integral_constant<int, 0>{}, 2);
+    step(i + 5, integral_constant<int, 2>{}, integral_constant<int, 1>{}, 2);
   }
-  for (; i < ntile; ++i) {
-    wait_vmcnt<0>();
-    barrier();
-    if (i + 1 < ntile) issue(i + 1, (i + 1) % NS);
-    compute(i % NS, i < nfull ? 2 : 1);
-  }
+  for (; i < ntile; ++i) step(i, i % NSW, i % NSH, i < nfull ? 2 : 1);
 
   // Statistics of each hidden row over this wave's 64 entries.  Accumulator
   // register r of tile (vt, t) holds entry 64*vw + 32*vt + 8*(r/4) + 4*hh +
