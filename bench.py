@@ -227,7 +227,8 @@ def suite(args):
     for name, kw in (("decode_b8_p2048_l32", {}), ("block256_b16_p1024", {}),
                      ("gen8k_b4_l256", dict(prefix_len=512)), ("gen8k_b4_l256", dict(prefix_len=8192)),
                      ("gen8k_b4_l256", dict(prefix_len=16128)), ("highbatch_b64_p4096_l64", {}),
-                     ("decode_l16", {}), ("decode_l1", {}), ("decode_b64_p4096_l1", {})):
+                     ("decode_l16", {}), ("decode_l1", {}), ("decode_b64_p4096_l1", {}),
+                     ("decode_b128_p2048_l1", {})):
         cfg = synth.get_config(name, **kw)
         attn_case(f"attn {name} P={cfg.prefix_len}", cfg)
 

@@ -143,10 +143,21 @@ tt_status plan_attn(long long B, int P, int L, int Hq, int Hkv, int D, tt_dtype 
     } else if (M < tt::kAttnMfmaBM) {
       // Fewer packed rows than one query tile (single-token and very short
       // blocks): the matrix work is light and the call is a stream of K/V.
-      // One 4-wave workgroup per CU streaming a longer key range moved the
-      // bytes faster than two groups per workgroup or two workgroups per CU.
-      plan->kgroups = 1;
-      target = kMfmaTargetWG / 2;
+      // When the query tiles fill 3/4 to all of the CUs once, two key groups
+      // per workgroup stream each tile's keys without splits (P2048 L1: 192
+      // tiles 37.1 vs 42.7 us, 224: 42.5 vs 45.5, 256: 47.4 vs 49.6); with
+      // more, 8-wave workgroups would need a second round (320 tiles: 81.6 vs
+      // 61.7), and with fewer, one 4-wave workgroup per CU streaming a split
+      // of the key range moved the bytes as fast or faster (B32 P8192 L1:
+      // 50.5 vs 52.3).
+      const long long cus = kMfmaTargetWG / 2;
+      if (base * 4 >= 3 * cus && base <= cus) {
+        plan->kgroups = 2;
+        target = 2 * base;   // one split
+      } else {
+        plan->kgroups = 1;
+        target = cus;
+      }
     } else {
       const long long s2 = std::min(cdiv(kMfmaTargetWG / 2, base), std::max(n_tiles / 4, 1LL));
       const bool short_groups = n_tiles / (2 * s2) <= 8;

@@ -120,6 +120,12 @@ CONFIGS: dict[str, Config] = {c.name: c for c in [
            n_kv_heads=2, head_dim=128, dtype="bf16", qkv_std=1.0, vocab=131072, logit_std=3.0,
            k=1, steps=1,
            description="supplementary: high-batch geometry at L1 (prefix-bound, 268 MB of K/V)"),
+    # The same 268 MB of cache K/V over twice the sequences at half the prefix:
+    # 256 (item, kv head) pairs, one query tile per CU, no key splits.
+    Config("decode_b128_p2048_l1", 9, batch=128, prefix_len=2048, block_len=1, n_q_heads=32,
+           n_kv_heads=2, head_dim=128, dtype="bf16", qkv_std=1.0, vocab=131072, logit_std=3.0,
+           k=1, steps=1,
+           description="supplementary: 128 single-token sequences at P2048 (prefix-bound, 268 MB of K/V)"),
 ]}
 
 # Prefix lengths of the 8K-generation workload: an isolated sweep, and the

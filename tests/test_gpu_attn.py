@@ -238,6 +238,7 @@ FULL = [
     ("decode_l16", {}, [4], [0, 31]),
     ("decode_l1", {}, [0, 7], [3, 20]),
     ("decode_b64_p4096_l1", {}, [0, 63], [1, 30]),
+    ("decode_b128_p2048_l1", {}, [0, 127], [2, 31]),
 ]
 
 
