@@ -170,3 +170,15 @@ def test_full_size_decode_sampled():
     mask = synth.initial_mask(cfg)
     say("full-size LM head: oracle on sequences 0 and 5")
     check(inp, mask, "top_k", "decode full size", seqs=[0, 5], k=cfg.k)
+
+
+def test_full_vocab_odd_width_sampled():
+    """Vocabulary 131072 with d_model 2720 (an odd multiple of 32, so the last
+    column stage holds 32 columns) over 2 x 40 positions (a ragged row tile);
+    the oracle checks one sequence."""
+    cfg = cfg_v()
+    inp = synth.lmhead_inputs(cfg, d_model=2720, seed=67, batch=2, block_len=40)
+    rng = np.random.default_rng(67)
+    mask = (rng.random((2, 40)) < 0.8).astype(np.uint8)
+    say("full-vocabulary LM head at d_model 2720: oracle on sequence 1")
+    check(inp, mask, "top_k", "V=131072 d=2720", seqs=[1], k=6)
