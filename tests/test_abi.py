@@ -111,6 +111,38 @@ def test_attn_workspace_query():
         tt.attn_workspace_bytes(1, 10, 4, 6, 4, 64, torch.float32)
 
 
+def _attn_splits(batch, prefix_len, block_len, n_q_heads=32, n_kv_heads=2, head_dim=128):
+    """Key splits of the launch plan, read back from the workspace size
+    (splits x rows x (D + 1) fp32 partials, each part rounded up to 256 B)."""
+    ws = tt.attn_workspace_bytes(batch, prefix_len, block_len, n_q_heads, n_kv_heads, head_dim,
+                                 torch.bfloat16)
+    if ws == 0:
+        return 1
+    rows = batch * n_q_heads * block_len
+    up = lambda x: (x + 255) // 256 * 256
+    for s in range(2, 4096):
+        if up(s * rows * head_dim * 4) + up(s * rows * 4) == ws:
+            return s
+    raise AssertionError(f"workspace size {ws} matches no split count")
+
+
+@pytest.mark.parametrize("shape,splits", [
+    # B, P, L at 32 q / 2 kv heads, D = 128.  Long blocks with at least one
+    # wave of query tiles per CU: no splits.
+    ((16, 1024, 256), 1), ((4, 16128, 256), 1), ((64, 4096, 64), 1),
+    # Decode geometry: one 4-wave group per workgroup and about one workgroup
+    # per CU of key splits (65 tiles of 32 keys: 4 splits of 17 tiles at L32,
+    # 8 at L16; at L1 the 16 requested splits of 5 tiles leave 13 non-empty).
+    ((8, 2048, 32), 4), ((8, 2048, 16), 8), ((8, 2048, 1), 13),
+    # Single-token blocks: query tiles filling 3/4 to all of the CUs once take
+    # two key groups and no split; 128 tiles take two key splits.
+    ((96, 2048, 1), 1), ((128, 2048, 1), 1), ((64, 4096, 1), 2),
+])
+def test_attn_launch_plan_splits(shape, splits):
+    # Guards the tuned launch plans against an unintended change of the rules.
+    assert _attn_splits(*shape) == splits
+
+
 def unmask_call(**kw):
     a = dict(logits=FAKE, mask=FAKE, k=4, tokens=FAKE, mask_out=FAKE, batch=1, L=16, V=1000,
              conf=None, pred=None, ws=FAKE, wsb=1 << 20, stream=None)
