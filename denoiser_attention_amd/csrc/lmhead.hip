@@ -57,10 +57,10 @@ constexpr int NSW = 3;                              // weight ring stages
 constexpr int NSH = 2;                              // hidden ring stages
 constexpr int KS = 64;                              // d_model columns per stage
 constexpr int ROWB = KS * 2;                        // bytes of one row of a stage (128)
-constexpr int W_TILE = kLmVocab * ROWB;             // 16 KB
-constexpr int H_TILE = kLmRows * ROWB;              // 16 KB
-constexpr int W_LOADS = W_TILE / 16 / kThreads;     // 2 direct loads per thread
-constexpr int H_LOADS = H_TILE / 16 / kThreads;     // 2
+constexpr int W_TILE = kLmVocab * ROWB;             // 32 KB
+constexpr int H_TILE = kLmRows * ROWB;              // 32 KB
+constexpr int W_LOADS = W_TILE / 16 / kThreads;     // 4 direct loads per thread
+constexpr int H_LOADS = H_TILE / 16 / kThreads;     // 4
 static_assert(kLmVocab == 64 * 4, "four 64-entry vocabulary ranges per workgroup");
 static_assert(kLmRows == 256 && KS == 64, "tile shape");
 constexpr int RING = NSW * W_TILE + NSH * H_TILE;   // 160 KB: one workgroup per CU
@@ -256,8 +256,10 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_stats_kernel(LmParams p, i
     compute(ws, hs, n_halves);
   };
   int i = 0;
-  // Steady state, unrolled by 6 (both rings' periods): constant slots.
-  for (; i + 6 < nfull; i += 6) {
+  // Steady state, unrolled by 6 (both rings' periods): constant slots.  The
+  // generic loop below takes only the last nfull % 6 full stages and a
+  // 32-column last stage.
+  for (; i + 6 <= nfull; i += 6) {
     step(i, integral_constant<int, 0>{}, integral_constant<int, 0>{}, 2);
     step(i + 1, integral_constant<int, 1>{}, integral_constant<int, 1>{}, 2);
     step(i + 2, integral_constant<int, 2>{}, integral_constant<int, 0>{}, 2);
