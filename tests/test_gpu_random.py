@@ -3,7 +3,10 @@ fp32, every kernel family and launch option, ragged shapes, capacity padding)
 and the unmask step under every selection rule (vocabulary sizes that are not
 multiples of 4, random masks).  The shapes are drawn once from a fixed seed,
 so the cases are the same on every run; each is small enough for the fp64
-oracle."""
+oracle.  TT_RANDOM_SCALE=n (default 1) draws n times as many cases of each
+kind; the first ones are the default cases."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -15,10 +18,12 @@ from test_gpu_select import MASK_ID, MODES, check_select, gpu_step, varied_logit
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+SCALE = max(1, int(os.environ.get("TT_RANDOM_SCALE", "1")))
 
 
 def attn_cases(n=48, seed=2024):
     rng = np.random.default_rng(seed)
+    n *= SCALE
     cases = []
     for i in range(n):
         fp32 = i % 8 == 7
@@ -57,8 +62,39 @@ def test_random_attention(case):
     check_attn(got, oracle_attn(inp), "fp32" if fp32 else "bf16", not out_f32, f"random {case}")
 
 
+def wave_layout_cases(n=12, seed=3131):
+    """bf16 D = 128 MFMA cases with 64-row waves or 8-wave tile streams."""
+    rng = np.random.default_rng(seed)
+    n *= SCALE
+    cases = []
+    for i in range(n):
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 4, 16]))
+        opt = {"rows_per_wave": 64} if i % 2 == 0 else {"stream_waves": 8}
+        cases.append((i, int(rng.integers(1, 4)), G * Hkv, Hkv, int(rng.integers(1, 71)),
+                      int(rng.integers(0, 301)), int(rng.choice([0, 1, 3])),
+                      bool(rng.integers(0, 2)), opt))
+    return cases
+
+
+@pytest.mark.parametrize("case", wave_layout_cases(), ids=lambda c: f"layout{c[0]}")
+def test_random_wave_layouts(case):
+    i, B, Hq, Hkv, L, P, splits, out_f32, opt = case
+    cfg = synth.get_config("decode_b8_p2048_l32").with_(batch=B, n_q_heads=Hq, n_kv_heads=Hkv,
+                                                        head_dim=128, prefix_len=P, block_len=L)
+    inp = synth.attn_inputs(cfg, seed=600 + i, prefix_cap=P + i % 3)
+    if P + i % 3 == 0:
+        inp["k_ctx"] = inp["k_ctx"].reshape(B, Hkv, 0, 128)
+    kw = dict(path="mfma", kv_splits=splits, **opt)
+    if out_f32:
+        kw["out_dtype"] = torch.float32
+    got = gpu_attn(inp, DEV, **kw)
+    check_attn(got, oracle_attn(inp), "bf16", not out_f32, f"random layout {case}")
+
+
 def unmask_cases(n=32, seed=77):
     rng = np.random.default_rng(seed)
+    n *= SCALE
     cases = []
     for i in range(n):
         B = int(rng.integers(1, 7))
@@ -93,6 +129,7 @@ def test_random_unmask(case):
 
 def varlen_cases(n=16, seed=4048):
     rng = np.random.default_rng(seed)
+    n *= SCALE
     cases = []
     for i in range(n):
         Hkv = int(rng.choice([1, 2]))
@@ -116,6 +153,7 @@ def test_random_varlen(case):
 
 def multiblock_cases(n=12, seed=5050):
     rng = np.random.default_rng(seed)
+    n *= SCALE
     cases = []
     for i in range(n):
         Hkv = int(rng.choice([1, 2]))
@@ -139,6 +177,7 @@ def test_random_multiblock(case):
 
 def lmhead_cases(n=10, seed=6060):
     rng = np.random.default_rng(seed)
+    n *= SCALE
     cases = []
     for i in range(n):
         mode = str(rng.choice(list(MODES)))
