@@ -11,6 +11,7 @@ set exceeds the 256 MB Infinity Cache and every step streams from HBM.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--graph]
     python bench.py --suite                      (supplementary workloads)
     python bench.py --attn-only --config NAME    (one attention workload, for counter runs)
+    python bench.py --lmhead-only                (the fused LM head workloads, for traces)
 
 The timed loop issues each step's three library calls on one stream.  With
 --graph each input set's step is captured once into a HIP graph and the loop
@@ -62,6 +63,9 @@ def parse_args():
     ap.add_argument("--attn-only", action="store_true",
                     help="instead of the step: only the attention call of --config "
                          "(and --prefix-len), timed as the suite times it (for counter runs)")
+    ap.add_argument("--lmhead-only", action="store_true",
+                    help="instead of the step: only the fused LM head workloads of the suite "
+                         "(256 and 4096 masked rows), for kernel traces")
     ap.add_argument("--kernel-reps", type=int, default=200,
                     help="back-to-back launches timed for the per-kernel roofline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -217,6 +221,39 @@ def suite(args):
              input_sets=n_sets)
         del keep, fns
 
+    def lmhead_section():
+        # Fused LM head + unmask vs the library GEMM + this unmask.
+        d = synth.LM_D_MODEL
+        for name, B, L in (("decode_b8", 8, 32), ("block256_b16", 16, 256)):
+            V = 131072
+            torch.manual_seed(0)
+            h = torch.randn(B, L, d, device=dev).to(torch.bfloat16)
+            w = (torch.randn(V, d, device=dev) * (3.0 / d ** 0.5)).to(torch.bfloat16)
+            mask = torch.ones((B, L), dtype=torch.uint8, device=dev)
+            tok = torch.zeros((B, L), dtype=torch.int32, device=dev)
+            mo = torch.empty_like(mask)
+            with torch.cuda.stream(stream):
+                call = tt.prepare_lmhead_unmask_step(h, w, mask, tt.select_rule("top_k", k=8), tok, mo,
+                                                     stream=stream)
+            us = time_calls([call], n=10)
+            rows = B * L
+            logits = torch.empty((rows, V), dtype=torch.float32, device=dev)
+            ws = torch.empty(tt.unmask_workspace_bytes(B, L, V), dtype=torch.uint8, device=dev)
+
+            def unfused():
+                logits.copy_(torch.matmul(h.view(rows, d), w.t()))
+                tt.unmask_step(logits.view(B, L, V), mask, 8, tok, mask_out=mo, workspace=ws,
+                               stream=stream)
+            us_u = time_calls([unfused], n=10)
+            emit(f"lmhead+unmask {name} rows={rows} V={V} d={d}", us, V * d * 2 + rows * d * 2,
+                 2.0 * rows * V * d, kind="fused LM head", unfused_library_gemm_us=us_u)
+            del h, w, logits
+
+
+    if args.lmhead_only:
+        lmhead_section()
+        return
+
     if args.attn_only:
         kw = {} if args.prefix_len is None else {"prefix_len": args.prefix_len}
         cfg = synth.get_config(args.config, **kw)
@@ -287,33 +324,7 @@ def suite(args):
         emit(f"unmask commit {mode} decode_b8", time_calls([c]), B * L * 16 * 16 + 2 * B * L, 0,
              kind="selection")
     del xs, reds
-
-    # Fused LM head + unmask vs the library GEMM + this unmask.
-    d = synth.LM_D_MODEL
-    for name, B, L in (("decode_b8", 8, 32), ("block256_b16", 16, 256)):
-        V = 131072
-        torch.manual_seed(0)
-        h = torch.randn(B, L, d, device=dev).to(torch.bfloat16)
-        w = (torch.randn(V, d, device=dev) * (3.0 / d ** 0.5)).to(torch.bfloat16)
-        mask = torch.ones((B, L), dtype=torch.uint8, device=dev)
-        tok = torch.zeros((B, L), dtype=torch.int32, device=dev)
-        mo = torch.empty_like(mask)
-        with torch.cuda.stream(stream):
-            call = tt.prepare_lmhead_unmask_step(h, w, mask, tt.select_rule("top_k", k=8), tok, mo,
-                                                 stream=stream)
-        us = time_calls([call], n=10)
-        rows = B * L
-        logits = torch.empty((rows, V), dtype=torch.float32, device=dev)
-        ws = torch.empty(tt.unmask_workspace_bytes(B, L, V), dtype=torch.uint8, device=dev)
-
-        def unfused():
-            logits.copy_(torch.matmul(h.view(rows, d), w.t()))
-            tt.unmask_step(logits.view(B, L, V), mask, 8, tok, mask_out=mo, workspace=ws,
-                           stream=stream)
-        us_u = time_calls([unfused], n=10)
-        emit(f"lmhead+unmask {name} rows={rows} V={V} d={d}", us, V * d * 2 + rows * d * 2,
-             2.0 * rows * V * d, kind="fused LM head", unfused_library_gemm_us=us_u)
-        del h, w, logits
+    lmhead_section()
 
 
 def main():
@@ -327,7 +338,7 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    if args.suite or args.attn_only:
+    if args.suite or args.attn_only or args.lmhead_only:
         suite(args)
         return
 
