@@ -136,3 +136,75 @@ def check_unmask(got: dict, ref: dict, mask: np.ndarray, k: int, tokens0: np.nda
                 assert c[committed].min() >= c[left].max() - GAP_EXEMPT
     say(f"{what}: conf max_abs={worst_conf:.3e} exempt={exempt}")
     return exempt
+
+
+def expected_commit_count(mode: str, n: int, L: int, gpu_conf_masked=None, **params) -> int:
+    """Committed count of one step under a selection rule (TwoTower paper
+    §2.2 "Sampling", Algorithm 2), from the rule's own arithmetic: exact for
+    top-k, leftmost and the schedule; for the threshold rule it is taken from
+    the GPU's own fp32 confidences (the kernel compares those with gamma)."""
+    if mode in ("top_k", "leftmost"):
+        return min(int(params["k"]), n)
+    if mode == "schedule":
+        T, r = int(params["n_steps"]), int(params["step"])
+        return max(0, n - (L * (T - r)) // T)
+    if mode == "threshold":
+        d = int(params["steps_left"])
+        above = int((np.asarray(gpu_conf_masked, np.float32) > np.float32(params["gamma"])).sum())
+        return min(n, max(-(-n // d), above))
+    raise ValueError(mode)
+
+
+def check_commit_valid(what: str, mode: str, mb: np.ndarray, committed: np.ndarray,
+                       gpu_conf: np.ndarray, ref_conf: np.ndarray, ref_commit: np.ndarray,
+                       tol: np.ndarray, exempt_slack: float, **params) -> bool:
+    """Validity of one sequence's commit set where floating point may decide it.
+
+    mb          masked positions (bool [L])
+    committed   positions the GPU committed (bool [L])
+    gpu_conf    the GPU's own fp32 confidences (conf_out)
+    ref_conf    the oracle's float64 confidences
+    ref_commit  the oracle's commit set
+    tol         per-position bound on |gpu_conf - ref_conf| (already asserted)
+    exempt_slack  a swapped pair (a, b) is accepted only when the oracle ranks
+                b above a by at most tol_a + tol_b + exempt_slack
+
+    Asserts: the count (exact; for the threshold rule equal to the count the
+    GPU's own confidences give, and inside the range the oracle's
+    confidences +- tol allow); the set is the first `count` positions of the
+    GPU's own ranking (conf desc, position asc; position asc for leftmost);
+    and, against the oracle, equality unless the boundary is a near tie by the
+    per-position tolerances (or, for the threshold rule, a confidence lies
+    within tol + exempt_slack of gamma).  Returns True if exempted."""
+    L = mb.shape[0]
+    pos = np.nonzero(mb)[0]
+    n = pos.size
+    n_got = int(committed.sum())
+    n_exp = expected_commit_count(mode, n, L, gpu_conf[pos], **params)
+    assert n_got == n_exp, f"{what}: count {n_got} != {n_exp}"
+    if mode == "threshold" and n:
+        d = int(params["steps_left"])
+        g = float(params["gamma"])
+        floor_n = -(-n // d)
+        lo = min(n, max(floor_n, int((ref_conf[pos] - tol[pos] > g).sum())))
+        hi = min(n, max(floor_n, int((ref_conf[pos] + tol[pos] > g).sum())))
+        assert lo <= n_got <= hi, f"{what}: threshold count {n_got} outside [{lo}, {hi}]"
+    # The committed set is a prefix of the GPU's own ranking.
+    if mode == "leftmost":
+        own = list(pos[:n_exp])
+    else:
+        own = sorted(pos.tolist(), key=lambda p: (-float(gpu_conf[p]), p))[:n_exp]
+    assert set(np.nonzero(committed)[0].tolist()) == set(int(p) for p in own), \
+        f"{what}: commit set is not a prefix of the GPU's own ranking"
+    if np.array_equal(committed, ref_commit):
+        return False
+    assert mode != "leftmost", f"{what}: leftmost set differs"
+    # Exempt only a near tie: every pair the two sets order differently is
+    # within the per-position tolerances of each other in the oracle.
+    extra = np.nonzero(committed & ~ref_commit)[0]
+    missing = np.nonzero(ref_commit & ~committed & mb)[0]
+    for a in extra:
+        for b in missing:
+            assert ref_conf[b] - ref_conf[a] <= tol[a] + tol[b] + exempt_slack, \
+                f"{what}: swapped pair ({a}, {b}) is not a near tie"
+    return True

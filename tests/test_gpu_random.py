@@ -124,7 +124,7 @@ def test_random_unmask(case):
     tokens0 = np.full((B, L), MASK_ID, np.int32)
     got = gpu_step(x, mask, tokens0, mode, split=split, **params)
     ref = oracle.unmask_step_select(x.astype(np.float64), mask, MODES[mode], **params)
-    check_select(got, ref, mask, tokens0, mode, f"random {case[:6]}")
+    check_select(got, ref, mask, tokens0, mode, f"random {case[:6]}", **params)
 
 
 def varlen_cases(n=16, seed=4048):
