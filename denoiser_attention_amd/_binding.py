@@ -7,6 +7,7 @@ or PyTorch fallback.  If the library is missing, every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -133,6 +134,13 @@ def _stream(device: torch.device, stream) -> int:
     return s.cuda_stream
 
 
+def _on(stream):
+    """Context in which the binding allocates its own workspaces and outputs:
+    the launch stream, so that the caching allocator never hands such a
+    buffer to another stream while a kernel on `stream` may still use it."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _require(cond: bool, msg: str) -> None:
     if not cond:
         raise ValueError(msg)
@@ -187,14 +195,16 @@ def block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, *, out=None, ou
         Pcap = k_ctx.shape[2]
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if out is None:
-        out = torch.empty((B, Hq, L, D), dtype=out_dtype, device=device)
+        with _on(stream):
+            out = torch.empty((B, Hq, L, D), dtype=out_dtype, device=device)
     _cuda_contig("out", out, device)
     _require(tuple(out.shape) == (B, Hq, L, D), "out must be [B, Hq, L, D]")
     opts = AttnOpts(_PATHS[path], kv_splits, kv_groups, rows_per_wave, stream_waves)
     need = attn_workspace_bytes(B, prefix_len, L, Hq, Hkv, D, q.dtype, path, kv_splits, kv_groups,
                                 rows_per_wave, stream_waves)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().tt_block_attn_ex(
         _ptr(q), _ptr(k_ctx), _ptr(v_ctx), prefix_len, _ptr(k_blk), _ptr(v_blk), L, Hq, Hkv, D,
@@ -240,14 +250,16 @@ def block_attn_varlen(q, k_ctx, v_ctx, prefix_lens, max_prefix_len, k_blk, v_blk
     Pcap = _ctx_checks(k_ctx, v_ctx, q, B, Hkv, D, device, max_prefix_len)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if out is None:
-        out = torch.empty((B, Hq, L, D), dtype=out_dtype, device=device)
+        with _on(stream):
+            out = torch.empty((B, Hq, L, D), dtype=out_dtype, device=device)
     _cuda_contig("out", out, device)
     _require(tuple(out.shape) == (B, Hq, L, D), "out must be [B, Hq, L, D]")
     opts = AttnOpts(_PATHS[path], kv_splits, kv_groups, rows_per_wave, stream_waves)
     need = attn_workspace_bytes(B, max_prefix_len, L, Hq, Hkv, D, q.dtype, path, kv_splits,
                                 kv_groups, rows_per_wave, stream_waves)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().tt_block_attn_varlen(
         _ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(prefix_lens), int(max_prefix_len), _ptr(k_blk),
@@ -294,14 +306,16 @@ def block_attn_multiblock(q, k_ctx, v_ctx, k_noisy, v_noisy, block_size, scale, 
     cap = _ctx_checks(k_ctx, v_ctx, q, B, Hkv, D, device, (N - 1) * S)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if out is None:
-        out = torch.empty((B, Hq, T, D), dtype=out_dtype, device=device)
+        with _on(stream):
+            out = torch.empty((B, Hq, T, D), dtype=out_dtype, device=device)
     _cuda_contig("out", out, device)
     _require(tuple(out.shape) == (B, Hq, T, D), "out must be [B, Hq, N*S, D]")
     opts = AttnOpts(_PATHS[path], kv_splits, kv_groups, rows_per_wave, stream_waves)
     need = attn_multiblock_workspace_bytes(B, S, N, Hq, Hkv, D, q.dtype, path, kv_splits,
                                            kv_groups, rows_per_wave, stream_waves)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().tt_block_attn_multiblock(
         _ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(k_noisy), _ptr(v_noisy), S, N, Hq, Hkv, D,
@@ -342,10 +356,12 @@ def unmask_step(logits, mask_state, k, tokens, *, mask_out=None, conf_out=None, 
     device, B, L = _unmask_checks(logits, mask_state, tokens, mask_out, conf_out, pred_out)
     V = logits.shape[2]
     if mask_out is None:
-        mask_out = torch.empty_like(mask_state)
+        with _on(stream):
+            mask_out = torch.empty_like(mask_state)
     need = unmask_workspace_bytes(B, L, V)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel()
     st = lib().tt_unmask_step(_ptr(logits), _ptr(mask_state), int(k), _ptr(tokens),
                               _ptr(mask_out), B, L, V, _ptr(conf_out), _ptr(pred_out),
@@ -360,10 +376,12 @@ def unmask_step_ex(logits, mask_state, select: Select, tokens, *, mask_out=None,
     device, B, L = _unmask_checks(logits, mask_state, tokens, mask_out, conf_out, pred_out)
     V = logits.shape[2]
     if mask_out is None:
-        mask_out = torch.empty_like(mask_state)
+        with _on(stream):
+            mask_out = torch.empty_like(mask_state)
     need = unmask_workspace_bytes(B, L, V)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel()
     st = lib().tt_unmask_step_ex(_ptr(logits), _ptr(mask_state), ctypes.byref(select),
                                  _ptr(tokens), _ptr(mask_out), B, L, V, _ptr(conf_out),
@@ -428,7 +446,8 @@ def prepare_block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, out, *,
     need = attn_workspace_bytes(B, prefix_len, L, Hq, Hkv, D, q.dtype, path, kv_splits, kv_groups,
                                 rows_per_wave, stream_waves)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
     # one validating call through the checked path
     block_attn(q, k_ctx, v_ctx, prefix_len, k_blk, v_blk, scale, out=out, path=path,
                kv_splits=kv_splits, kv_groups=kv_groups, rows_per_wave=rows_per_wave,
@@ -494,10 +513,12 @@ def _lmhead_args(hidden, weight, mask_state, select, tokens, mask_out, conf_out,
     V, d = weight.shape
     _require(hidden.shape[2] == d, "weight: [vocab, d_model] with the hidden width")
     if mask_out is None:
-        mask_out = torch.empty_like(mask_state)
+        with _on(stream):
+            mask_out = torch.empty_like(mask_state)
     need = lmhead_unmask_workspace_bytes(B, L, V, d)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        with _on(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel()
     sel = Select(select.mode, select.k, select.gamma, select.steps_left, select.step,
                  select.n_steps)

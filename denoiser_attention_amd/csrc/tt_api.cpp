@@ -206,6 +206,10 @@ tt_status plan_attn(long long B, int P, int L, int Hq, int Hkv, int D, tt_dtype 
 
 tt_status to_status(hipError_t e) { return e == hipSuccess ? TT_OK : TT_EHIP; }
 
+// The attention and LM-head kernels move tiles with 16-byte loads and stores
+// (and direct-to-LDS loads) from each tensor's base address.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 struct UnmaskPlan {
   int n_chunks = 0;
   int chunk = 0;
@@ -294,6 +298,12 @@ tt_status attn_run(const AttnCall& c) {
   if (c.Pcap > 0 && (!c.k_ctx || !c.v_ctx)) return TT_EINVAL;
   if (c.prefix_mode == 1 && !c.prefix_lens) return TT_EINVAL;
   if (plan.ws_bytes > 0 && (!c.workspace || c.workspace_bytes < plan.ws_bytes)) return TT_EINVAL;
+  if (!aligned16(c.q) || !aligned16(c.k_ctx) || !aligned16(c.v_ctx) || !aligned16(c.k_blk) ||
+      !aligned16(c.v_blk) || !aligned16(c.out))
+    return TT_EINVAL;
+  if (plan.ws_bytes > 0 && !aligned16(c.workspace)) return TT_EINVAL;
+  if (c.prefix_mode == 1 && (reinterpret_cast<uintptr_t>(c.prefix_lens) & 3u) != 0)
+    return TT_EINVAL;
   st = device_present();
   if (st != TT_OK) return st;
 
@@ -610,6 +620,7 @@ TT_EXPORT tt_status tt_lmhead_unmask_step(const void* hidden, const void* weight
   if (st != TT_OK || plan.empty) return st;
   if (!hidden || !weight || !mask_state || !tokens_out || !mask_out) return TT_EINVAL;
   if (!workspace || workspace_bytes < plan.ws_bytes) return TT_EINVAL;
+  if (!aligned16(hidden) || !aligned16(weight) || !aligned16(workspace)) return TT_EINVAL;
   st = device_present();
   if (st != TT_OK) return st;
   char* ws = static_cast<char*>(workspace);
@@ -640,3 +651,4 @@ TT_EXPORT tt_status tt_lmhead_unmask_step(const void* hidden, const void* weight
   if (e != hipSuccess) return TT_EHIP;
   return to_status(tt::launch_topk_commit(up, stream));
 }
+

@@ -27,6 +27,13 @@
  *     compiled kernels do not cover returns TT_EUNSUPPORTED.  No visible HIP
  *     device returns TT_ENODEV.  A failed launch returns TT_EHIP.  Faults inside
  *     a kernel surface at the caller's stream synchronisation.
+ *   - The attention and LM-head entry points move tiles with 16-byte loads and
+ *     stores from each tensor's base: q, k_ctx, v_ctx, k_blk, v_blk, out,
+ *     hidden, weight and any workspace must be 16-byte aligned (prefix_lens
+ *     4-byte aligned), else TT_EINVAL.  A contiguous torch tensor that starts
+ *     its own allocation is always aligned; a view at an odd element offset
+ *     may not be.  The unmask entry points accept logits at any 4-byte
+ *     alignment.
  *   - Workspaces are caller-provided device memory of at least the size the
  *     matching *_workspace_bytes query returns (NULL is allowed when it returns
  *     0).  Two calls that run concurrently must not share a workspace.
@@ -92,7 +99,10 @@ const char* tt_version(void);
 
 /* Bytes of workspace tt_block_attn / tt_block_attn_ex need for this shape and
  * these options (opts may be NULL = defaults).  Returns 0 when no workspace is
- * needed, and SIZE_MAX when the arguments are invalid. */
+ * needed, and SIZE_MAX when the arguments are invalid.
+ * Additions to the query the path's definition names (batch and the shape):
+ * dtype, because the kernel family and its split plan depend on it, and opts,
+ * the tuning knobs of tt_block_attn_ex (NULL for tt_block_attn). */
 size_t tt_block_attn_workspace_bytes(int batch, int prefix_len, int block_len, int n_q_heads,
                                      int n_kv_heads, int head_dim, tt_dtype dtype,
                                      const tt_attn_opts* opts);
@@ -121,8 +131,17 @@ size_t tt_block_attn_workspace_bytes(int batch, int prefix_len, int block_len, i
  *   prefix_cap  allocated cache rows per (b, kv head), >= prefix_len
  *   dtype       TT_FP32 or TT_BF16 for q/k/v (fp32 accumulation either way)
  *   out_dtype   dtype, or TT_FP32 for bf16 inputs
+ *   workspace, workspace_bytes  see tt_block_attn_workspace_bytes (opts NULL)
+ *   stream      HIP stream the kernels are enqueued on (0 = null stream)
  * Inputs are read only.  The call is deterministic: the same inputs give the
- * same output bits. */
+ * same output bits.
+ * Arguments beyond the path's named signature (q, k_ctx, v_ctx, prefix_len,
+ * k_blk, v_blk, block_len, n_q_heads, n_kv_heads, head_dim, scale, out), all
+ * after it so that its order is kept: batch (the named form is per sequence);
+ * prefix_cap (the cache's capacity stride: a growing cache is allocated once);
+ * dtype and out_dtype (bf16 or fp32 inputs; fp32 output for bf16 inputs);
+ * workspace and workspace_bytes (key-split partials: the library never
+ * allocates); stream. */
 tt_status tt_block_attn(const void* q, const void* k_ctx, const void* v_ctx, int prefix_len,
                         const void* k_blk, const void* v_blk, int block_len, int n_q_heads,
                         int n_kv_heads, int head_dim, float scale, void* out, int batch,
@@ -207,7 +226,14 @@ size_t tt_unmask_workspace_bytes(int batch, int block_len, int vocab);
  *               -1 elsewhere (NULL = not written)
  *   pred_out    optional [batch, block_len] int32: pred at masked positions,
  *               -1 elsewhere (NULL = not written)
- * The call is deterministic. */
+ *   workspace, workspace_bytes  at least tt_unmask_workspace_bytes(batch,
+ *               block_len, vocab) bytes: the per-chunk vocabulary partials
+ *   stream      HIP stream the kernels are enqueued on (0 = null stream)
+ * The call is deterministic.
+ * Arguments beyond the path's named signature (logits, mask_state, k,
+ * tokens_out, mask_out), all after it: batch, block_len and vocab (the sizes
+ * of logits[B,L,V]); conf_out and pred_out (diagnostics, NULL = not
+ * written); workspace and workspace_bytes; stream. */
 tt_status tt_unmask_step(const float* logits, const uint8_t* mask_state, int k,
                          int32_t* tokens_out, uint8_t* mask_out, int batch, int block_len,
                          int vocab, float* conf_out, int32_t* pred_out, void* workspace,

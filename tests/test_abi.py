@@ -302,3 +302,25 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         B.lib()
+
+
+@pytest.mark.parametrize("field", ["q", "k_ctx", "v_ctx", "k_blk", "v_blk", "out"])
+def test_attn_rejects_misaligned_tensor(field):
+    # 16-byte tile loads and stores from every tensor's base: an offset view
+    # is refused before anything is enqueued.
+    assert attn_call(**{field: FAKE + 8}, ws=FAKE, wsb=1 << 24) == B.TT_EINVAL
+    assert attn_call(**{field: FAKE + 2}, dtype=B.TT_BF16, odt=B.TT_BF16, ws=FAKE,
+                     wsb=1 << 24) == B.TT_EINVAL
+
+
+def test_attn_rejects_misaligned_workspace_and_lengths():
+    decode = dict(dtype=B.TT_BF16, odt=B.TT_BF16, hq=32, hkv=2, d=128, prefix_len=2048,
+                  pcap=2048, block_len=32, batch=8)
+    assert attn_call(**decode, ws=FAKE + 4, wsb=1 << 26) == B.TT_EINVAL
+    assert varlen_call(lens=FAKE + 2) == B.TT_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(h=FAKE + 2), dict(w=FAKE + 8), dict(ws=FAKE + 4)])
+def test_lmhead_rejects_misaligned(kw):
+    assert lmhead_call(**kw) == B.TT_EINVAL
+
