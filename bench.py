@@ -4,24 +4,27 @@ A step is one pass of the whole hot path over one batch of synthetic input:
 the block attention of one denoiser attention layer (tt_block_attn) and the
 confidence-unmask step (tt_unmask_reduce + tt_unmask_commit, which together
 are tt_unmask_step), at the first refinement step of a block (every position
-still masked, the most logits to read).  Inputs are resident in HBM before
-timing starts; several independent input sets are rotated so that the working
-set exceeds the 256 MB Infinity Cache and every step streams from HBM.
+still masked, the most logits to read).  The default workload is the largest
+single-GPU configuration: 64 sequences, prefix 4096, block 64, 32 query / 2 KV
+heads, head_dim 128, bf16, vocabulary 131072 (4096 masked positions).
+Inputs are resident in HBM before timing starts; independent input sets are
+rotated so that the working set exceeds the 256 MB Infinity Cache and every
+step streams from HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--graph]
     python bench.py --suite                      (supplementary workloads)
     python bench.py --attn-only --config NAME    (one attention workload, for counter runs)
     python bench.py --lmhead-only                (the fused LM head workloads, for traces)
 
-The timed loop issues each step's three library calls on one stream.  With
---graph each input set's step is captured once into a HIP graph and the loop
-replays the graphs instead (checked bit for bit against an eager step; on
-this stack the replays have measured slower than the eager calls).
+Before the W warm-up steps, the step runs untimed for --prewarm-ms of wall
+time: after the idle spell of input setup the GPU's clocks need about 20 ms
+of load to ramp up, so the timed steps see steady clocks whatever W is.
 
-Prints ONE JSON line: block-tokens/s over the timed steps, the roofline of the
-dominant kernel (the vocabulary pass, HBM-bound; its duration from HIP events
-around a back-to-back loop of that kernel alone on the launch stream), the
-attention call measured the same way, and the CPU oracle timed on the host.
+Prints ONE JSON line: block-tokens/s over the timed steps; the roofline of
+the dominant kernel of the step (the one with the longest average launch,
+timed by HIP events around a back-to-back loop of that kernel alone on the
+launch stream); both kernels' figures; and the CPU oracle timed on a bounded
+sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -39,17 +42,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix, published
 METRIC = "denoised block-tokens/s per denoising step; % HBM/MFMA peak"
-DEFAULT_CONFIG = "decode_b8_p2048_l32"
+DEFAULT_CONFIG = "highbatch_b64_p4096_l64"
 PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    # The GPU's clocks ramp up over the first ~20 ms of load after an idle
-    # spell (input setup): 2000 warm-up steps (~0.1 s) time the steady state.
-    ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prewarm-ms", type=float, default=200.0,
+                    help="untimed steps for this much wall time before the warm-up steps "
+                         "(the clocks ramp up over the first ~20 ms of load)")
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--prefix-len", type=int, default=None)
     ap.add_argument("--rotate", type=int, default=0, help="input sets rotated (0 = auto)")
@@ -88,60 +92,106 @@ def copy_calibration():
     print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": 4}}))
 
 
-def kernel_source_digest() -> str:
-    """Digest of the vocabulary-pass kernel source; counter-derived traffic is
-    only reported while it matches the digest recorded with the counters."""
-    with open(os.path.join(ROOT, "denoiser_attention_amd", "csrc", "unmask.hip"), "rb") as fh:
+# Kernel -> source file whose digest keys its committed counter profile.
+KERNEL_SOURCES = {"vocab_reduce": "unmask.hip", "attn_mfma": "attn_mfma.hip"}
+
+
+def kernel_source_digest(kernel: str = "vocab_reduce") -> str:
+    """Digest of a kernel's source file; counter-derived traffic is only
+    reported while it matches the digest recorded with the counters."""
+    path = os.path.join(ROOT, "denoiser_attention_amd", "csrc", KERNEL_SOURCES[kernel])
+    with open(path, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per launch of the vocabulary pass from the committed rocprofv3
-    --pmc summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel factor),
-    or None when absent or taken on a different kernel source."""
-    path = os.path.join(PROFILES, f"vocab_reduce_{workload}_traffic.md")
+def recorded_traffic(workload: str, kernel: str = "vocab_reduce"):
+    """HBM bytes per launch of `kernel` at `workload` from the committed
+    rocprofv3 --pmc summary profiles/<kernel>_<workload>_traffic.md
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel factor), or None when
+    absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     d = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    if not m or not d or d.group(1) != kernel_source_digest():
+    if not m or not d or d.group(1) != kernel_source_digest(kernel):
         return None
     return float(m.group(1))
 
 
-def cpu_baseline(cfg, host_sets, mask, min_seconds=10.0):
-    """The oracle as it stands, on the host cores, over whole steps of the same
-    workload (all heads of the attention call, all masked rows), repeated over
-    the rotated input sets until about min_seconds have passed."""
+def host_cores() -> int:
+    """Host cores this process may use, capped at 16 (the CPU share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _oracle_unmask_seq(task):
+    """Worker: the oracle's unmask step on one sequence; returns its seconds."""
+    import oracle
+    x, m, k = task
+    t0 = time.perf_counter()
+    oracle.unmask_step(x, m, k)
+    return time.perf_counter() - t0
+
+
+def _worker_ready(_):
+    import oracle  # noqa: F401
+    return os.getpid()
+
+
+def cpu_baseline(cfg, inp, lg, mask, attn_seqs=8, unmask_seqs=16):
+    """The oracle as it stands, timed on the host cores over a bounded sample of
+    one step of the workload, scaled to the whole step:
+      attention: every query head of the first `attn_seqs` sequences, numpy
+        fp64 with BLAS on the host cores; scaled by batch / attn_seqs;
+      unmask: the first `unmask_seqs` sequences (every masked row, then the
+        per-sequence top-k), one sequence per task in a pool of one process
+        per host core (wall time of the pool, transfers included); scaled by
+        batch / unmask_seqs.
+    Runs before the process touches the GPU (the pool's workers are spawned
+    interpreters that load only numpy and the oracle)."""
+    import multiprocessing as mp
+
     import threadpoolctl
 
     import oracle
-    blas = [i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
-            if i.get("user_api") == "blas"]
-    threads = max(blas) if blas else 1
-    f = lambda a: oracle.decode_bf16(a) if a.dtype == np.uint16 else a.astype(np.float64)
-    t_attn = t_unmask = 0.0
-    steps = 0
-    while steps < len(host_sets) and (steps == 0 or t_attn + t_unmask < min_seconds):
-        inp, lg = host_sets[steps]
-        t0 = time.perf_counter()
-        oracle.block_attn(f(inp["q"]), f(inp["k_ctx"]), f(inp["v_ctx"]), inp["prefix_len"],
-                          f(inp["k_blk"]), f(inp["v_blk"]), inp["scale"])
-        t_attn += time.perf_counter() - t0
-        t0 = time.perf_counter()
-        oracle.unmask_step(lg, mask, cfg.k)
-        t_unmask += time.perf_counter() - t0
-        steps += 1
-    t_step = (t_attn + t_unmask) / steps
+    cores = host_cores()
     B, L = mask.shape
+    f = lambda a: oracle.decode_bf16(a) if a.dtype == np.uint16 else a.astype(np.float64)
+    na = min(attn_seqs, B)
+    with threadpoolctl.threadpool_limits(limits=cores, user_api="blas"):
+        blas = [i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()
+                if i.get("user_api") == "blas"]
+        args = [f(inp[n][:na]) for n in ("q", "k_ctx", "v_ctx", "k_blk", "v_blk")]
+        t0 = time.perf_counter()
+        oracle.block_attn(args[0], args[1], args[2], inp["prefix_len"], args[3], args[4],
+                          inp["scale"])
+        t_attn = time.perf_counter() - t0
+    nu = min(unmask_seqs, B)
+    tasks = [(lg[b:b + 1], mask[b:b + 1], cfg.k) for b in range(nu)]
+    with mp.get_context("spawn").Pool(processes=cores) as pool:
+        pool.map(_worker_ready, range(cores))
+        t0 = time.perf_counter()
+        per_seq = pool.map(_oracle_unmask_seq, tasks, chunksize=1)
+        t_unmask = time.perf_counter() - t0
+    t_step = t_attn * B / na + t_unmask * B / nu
+    rows = int(mask[:nu].sum())
     return {
-        "value": B * L / t_step, "unit": "block-tokens/s", "cores": threads, "kind": "oracle",
-        "sample": (f"{steps} full steps of {cfg.name} (distinct input sets): attention over all "
-                   f"{cfg.batch}x{cfg.n_q_heads} (batch, head) pairs in numpy fp64 "
-                   f"({t_attn:.2f} s, BLAS threads={threads}), unmask of all {int(mask.sum())} "
-                   f"masked rows per step ({t_unmask:.2f} s, one thread)"),
+        "value": B * L / t_step, "unit": "block-tokens/s", "cores": cores, "kind": "oracle",
+        "sample": (f"one step of {cfg.name}: attention of sequences 0..{na - 1} (all "
+                   f"{cfg.n_q_heads} query heads) in numpy fp64, {t_attn:.2f} s with BLAS "
+                   f"threads={max(blas) if blas else 1}, scaled x{B / na:g}; unmask of "
+                   f"sequences 0..{nu - 1} ({rows} masked rows of {cfg.vocab} logits), "
+                   f"{t_unmask:.2f} s wall in {cores} worker processes "
+                   f"({sum(per_seq):.1f} s of worker time), scaled x{B / nu:g}"),
+        "cores_per_leg": {"attention_blas_threads": max(blas) if blas else 1,
+                          "unmask_processes": cores},
         "seconds": t_attn + t_unmask,
+        "step_seconds_scaled": t_step,
     }
 
 
@@ -342,17 +392,9 @@ def main():
         suite(args)
         return
 
-    import torch
-
     sys.path.insert(0, ROOT)
-    import denoiser_attention_amd as tt
     from denoiser_attention_amd import synth
 
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     kw = {} if args.prefix_len is None else {"prefix_len": args.prefix_len}
     cfg = synth.get_config(args.config, **kw)
     B, L, V = cfg.batch, cfg.block_len, cfg.vocab
@@ -366,22 +408,37 @@ def main():
     R = args.rotate or max(2, int(np.ceil(1.0e9 / set_bytes)))
     R = min(R, 8)
 
+    # Host inputs of the first set; the CPU oracle is timed on them before the
+    # process touches the GPU.
+    first = (synth.attn_inputs(cfg, seed=0, step=0), synth.logits(cfg, seed=0, step=0))
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, first[0], first[1], np.ones((B, L), np.uint8))
+
+    import torch
+
+    import denoiser_attention_amd as tt
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
     def up(a):
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
     sets = []
-    host_sets = []
     for r in range(R):
-        inp = synth.attn_inputs(cfg, seed=0, step=r)
-        lg = synth.logits(cfg, seed=0, step=r)
-        if r < 3 and not args.no_cpu_baseline:
-            host_sets.append((inp, lg))
+        inp, lg = first if r == 0 else (synth.attn_inputs(cfg, seed=0, step=r),
+                                          synth.logits(cfg, seed=0, step=r))
         t = {n: up(inp[n]) for n in ("q", "k_ctx", "v_ctx", "k_blk", "v_blk")}
         t["logits"] = up(lg)
         sets.append(t)
-        del lg
+        del inp, lg
+    del first
     mask = torch.ones((B, L), dtype=torch.uint8, device=dev)
     mask_out = torch.empty_like(mask)
     tokens = torch.full((B, L), -1, dtype=torch.int32, device=dev)
@@ -427,6 +484,16 @@ def main():
         else:
             graphs[i % R].replay()
 
+    # Untimed pre-warm for a fixed wall time (clock ramp), then W warm-up steps.
+    prewarm_steps = 0
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        while (time.perf_counter() - t0) * 1e3 < args.prewarm_ms:
+            for _ in range(4):
+                step(prewarm_steps)
+                prewarm_steps += 1
+            stream.synchronize()
+    prewarm_s = time.perf_counter() - t0
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             step(i)
@@ -470,8 +537,8 @@ def main():
 
     def kernel_loop_us(which):
         """Average duration of one launch of call `which` (0 attention, 1
-        vocabulary pass) over back-to-back launches on rotated input sets,
-        between two HIP events on the launch stream."""
+        vocabulary pass, 2 commit) over back-to-back launches on rotated input
+        sets, between two HIP events on the launch stream."""
         n = args.kernel_reps
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -487,12 +554,56 @@ def main():
 
     reduce_us = kernel_loop_us(1)
     attn_us = kernel_loop_us(0)
+    commit_us = kernel_loop_us(2)
 
     n_masked = B * L
     reduce_bytes = n_masked * V * 4 + B * L          # masked logit rows + mask bytes
-    achieved_gbs = reduce_bytes / (reduce_us * 1e-6) / 1e9
+    reduce_gbs = reduce_bytes / (reduce_us * 1e-6) / 1e9
     attn_tflops = attn_flops / (attn_us * 1e-6) / 1e12
-    attn_t_roof = max(attn_bytes / (HBM_PEAK_GBS * 1e9), attn_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    attn_t_roof, attn_bound = _roof(attn_bytes, attn_flops)
+    attn_mfma = attn_bound == "mfma"
+
+    vocab_line = {
+        "kernel": "vocab_reduce_kernel (tt_unmask_reduce)", "avg_launch_us": reduce_us,
+        "bound": "hbm", "GBps": reduce_gbs, "frac": reduce_gbs / HBM_PEAK_GBS,
+        "algorithmic_bytes_per_launch": reduce_bytes,
+        "traffic": recorded_traffic(cfg.name, "vocab_reduce"),
+    }
+    attn_line = {
+        "kernel": "attn_mfma_kernel (+ split merge when planned) (tt_block_attn)",
+        "avg_call_us": attn_us, "tflops": attn_tflops,
+        "mfma_frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "bound": attn_bound,
+        "roof_us": attn_t_roof * 1e6, "roof_frac": attn_t_roof * 1e6 / attn_us,
+        "algorithmic_bytes": attn_bytes, "flops": attn_flops,
+        "workspace_bytes": attn_ws_n,
+        "traffic": recorded_traffic(cfg.name, "attn_mfma") if attn_ws_n == 0 else None,
+    }
+    timing = (f"HIP events around {args.kernel_reps} back-to-back launches on the launch "
+              "stream, rotated input sets")
+    if reduce_us >= attn_us:
+        roofline = {
+            "kernel": vocab_line["kernel"], "bound": "hbm", "achieved": reduce_gbs,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": reduce_gbs / HBM_PEAK_GBS,
+            "traffic": vocab_line["traffic"], "algorithmic_bytes_per_launch": reduce_bytes,
+            "avg_launch_us": reduce_us, "timing": timing,
+        }
+    elif attn_mfma:
+        roofline = {
+            "kernel": attn_line["kernel"], "bound": "mfma", "achieved": attn_tflops,
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": attn_line["traffic"],
+            "algorithmic_flops_per_launch": attn_flops,
+            "algorithmic_bytes_per_launch": attn_bytes, "avg_launch_us": attn_us,
+            "timing": timing,
+        }
+    else:
+        gbs = attn_bytes / (attn_us * 1e-6) / 1e9
+        roofline = {
+            "kernel": attn_line["kernel"], "bound": "hbm", "achieved": gbs,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "traffic": attn_line["traffic"], "algorithmic_bytes_per_launch": attn_bytes,
+            "avg_launch_us": attn_us, "timing": timing,
+        }
 
     result = {
         "metric": METRIC,
@@ -506,36 +617,27 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16+fp32" if cfg.dtype == "bf16" else "fp32",
-        "data": "synthetic (seeded N(0,1) Q/K/V, N(0,3) logits with planted peaks; "
-                f"{R} input sets rotated)",
+        "data": ("synthetic (seeded N(0,1) Q/K/V"
+                 + (", 1% K/V outlier channels x10" if cfg.outlier_frac else "")
+                 + ", N(0,3) logits"
+                 + (" with planted peaks" if cfg.plant_peaks else "")
+                 + (", 5% injected ties" if cfg.tie_frac else "")
+                 + f"; {R} input sets rotated)"),
         "config": {
             "workload": cfg.name, "batch": B, "prefix_len": P, "block_len": L,
             "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "vocab": V, "k": cfg.k,
             "masked_positions": n_masked, "attention_layers_per_step": 1,
             "parallelism": "single GPU",
         },
-        "roofline": {
-            "kernel": "vocab_reduce_kernel (tt_unmask_reduce)",
-            "bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved_gbs / HBM_PEAK_GBS,
-            "traffic": recorded_traffic(cfg.name),
-            "algorithmic_bytes_per_launch": reduce_bytes,
-            "avg_launch_us": reduce_us,
-            "timing": f"HIP events around {args.kernel_reps} back-to-back launches on the "
-                      "launch stream",
-        },
-        "attention": {
-            "avg_call_us": attn_us, "tflops": attn_tflops,
-            "mfma_frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
-            "roof_us": attn_t_roof * 1e6, "roof_frac": attn_t_roof * 1e6 / attn_us,
-            "algorithmic_bytes": attn_bytes, "flops": attn_flops,
-        },
+        "roofline": roofline,
+        "attention": attn_line,
+        "vocab_pass": vocab_line,
+        "commit_us": commit_us,
+        "prewarm": {"seconds": prewarm_s, "steps": prewarm_steps},
         "step_launch": "HIP graph replay per step" if graphs is not None else "eager calls",
         "graph_check": graph_check,
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, host_sets, np.ones((B, L), np.uint8))
     print(json.dumps(result), flush=True)
 
 

@@ -28,3 +28,22 @@ def test_help_lists_every_mode():
                  "--lmhead-only", "--kernel-reps", "--copy-calibration", "--no-cpu-baseline",
                  "--graph"):
         assert flag in r.stdout, flag
+
+
+def test_cpu_baseline_sample_on_host():
+    """The oracle leg of the bench on a small workload: a bounded sample,
+    scaled to one step, with the cores of each leg stated."""
+    sys.path.insert(0, ROOT)
+    import numpy as np
+
+    import bench
+    from denoiser_attention_amd import synth
+    cfg = synth.get_config("tiny_fp32").with_(batch=3)
+    inp = synth.attn_inputs(cfg, seed=0)
+    lg = synth.logits(cfg, seed=0)
+    res = bench.cpu_baseline(cfg, inp, lg, np.ones((3, cfg.block_len), np.uint8), attn_seqs=2,
+                             unmask_seqs=2)
+    assert res["kind"] == "oracle" and res["unit"] == "block-tokens/s"
+    assert res["value"] > 0 and res["cores"] >= 1
+    assert res["cores_per_leg"]["unmask_processes"] == res["cores"]
+    assert "scaled x1.5" in res["sample"]
