@@ -8,6 +8,7 @@ synthetic-input generator (``synth``).
     block_attn_varlen(..., prefix_lens, max_prefix_len, ...)       -> out (per-sequence prefix)
     block_attn_multiblock(q, k_ctx, v_ctx, k_noisy, v_noisy, S, scale) -> out (all noisy blocks)
     unmask_step(logits, mask_state, k, tokens)                     -> (tokens, mask_out)
+    unmask_step_noalloc(logits, mask_state, k, tokens)             -> (tokens, mask_out) (no workspace)
     unmask_step_ex(logits, mask_state, select_rule(...), tokens)   -> (tokens, mask_out)
     lmhead_unmask_step(hidden, weight, mask_state, select, tokens) -> (tokens, mask_out)
 """
@@ -17,7 +18,7 @@ from ._binding import (  # noqa: F401
     lmhead_unmask_step, lmhead_unmask_workspace_bytes, prepare_lmhead_unmask_step,
     prepare_block_attn, prepare_unmask_commit, prepare_unmask_commit_ex, prepare_unmask_reduce,
     select_rule, status_string, unmask_commit, unmask_commit_ex, unmask_reduce, unmask_step,
-    unmask_step_ex, unmask_workspace_bytes, version,
+    unmask_step_ex, unmask_step_noalloc, unmask_workspace_bytes, version,
 )
 
 __all__ = [
@@ -25,5 +26,6 @@ __all__ = [
     "attn_workspace_bytes", "block_attn", "block_attn_multiblock", "block_attn_varlen",
     "lmhead_unmask_step", "lmhead_unmask_workspace_bytes", "prepare_lmhead_unmask_step", "lib", "prepare_block_attn", "prepare_unmask_commit", "prepare_unmask_commit_ex",
     "prepare_unmask_reduce", "select_rule", "status_string", "unmask_commit", "unmask_commit_ex",
-    "unmask_reduce", "unmask_step", "unmask_step_ex", "unmask_workspace_bytes", "version",
+    "unmask_reduce", "unmask_step", "unmask_step_ex", "unmask_step_noalloc",
+    "unmask_workspace_bytes", "version",
 ]

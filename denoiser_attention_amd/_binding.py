@@ -21,6 +21,7 @@ TT_FP32, TT_BF16 = 0, 1
 TT_ATTN_AUTO, TT_ATTN_MFMA, TT_ATTN_SHUFFLE = 0, 1, 2
 _PATHS = {"auto": TT_ATTN_AUTO, "mfma": TT_ATTN_MFMA, "shuffle": TT_ATTN_SHUFFLE}
 SIZE_MAX = ctypes.c_size_t(-1).value
+NOALLOC_SCRATCH_BYTES = 8 << 20     # TT_NOALLOC_SCRATCH_BYTES
 
 
 class TTError(RuntimeError):
@@ -77,6 +78,7 @@ _SIGNATURES = {
                                    _vp, _vp, _vp, _sz, _vp]),
     "tt_unmask_workspace_bytes": (_sz, [_i, _i, _i]),
     "tt_unmask_step": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "tt_unmask_step_noalloc": (_i, [_vp, _vp, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
     "tt_unmask_reduce": (_i, [_vp, _vp, _i, _i, _i, _vp, _sz, _vp]),
     "tt_unmask_commit": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "tt_unmask_step_ex": (_i, [_vp, _vp, ctypes.POINTER(Select), _vp, _vp, _i, _i, _i, _vp, _vp,
@@ -367,6 +369,23 @@ def unmask_step(logits, mask_state, k, tokens, *, mask_out=None, conf_out=None, 
                               _ptr(mask_out), B, L, V, _ptr(conf_out), _ptr(pred_out),
                               _ptr(workspace), ws_bytes, _stream(device, stream))
     _check(st, "tt_unmask_step")
+    return tokens, mask_out
+
+
+def unmask_step_noalloc(logits, mask_state, k, tokens, *, mask_out=None, conf_out=None,
+                        pred_out=None, stream=None):
+    """tt_unmask_step_noalloc: tt_unmask_step with the library's static
+    device scratch in place of a workspace (no allocation in the library;
+    pass ``mask_out`` to allocate nothing here either)."""
+    device, B, L = _unmask_checks(logits, mask_state, tokens, mask_out, conf_out, pred_out)
+    V = logits.shape[2]
+    if mask_out is None:
+        with _on(stream):
+            mask_out = torch.empty_like(mask_state)
+    st = lib().tt_unmask_step_noalloc(_ptr(logits), _ptr(mask_state), int(k), _ptr(tokens),
+                                      _ptr(mask_out), B, L, V, _ptr(conf_out), _ptr(pred_out),
+                                      _stream(device, stream))
+    _check(st, "tt_unmask_step_noalloc")
     return tokens, mask_out
 
 

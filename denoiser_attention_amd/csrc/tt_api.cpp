@@ -2,10 +2,12 @@
 // workspace layout, and launches on the caller's stream.  The public contract
 // is include/tt.h.  Nothing here allocates device memory.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "tt.h"
 #include "tt_internal.h"
@@ -652,3 +654,71 @@ TT_EXPORT tt_status tt_lmhead_unmask_step(const void* hidden, const void* weight
   return to_status(tt::launch_topk_commit(up, stream));
 }
 
+// ---------------------------------------------------------------------------
+// tt_unmask_step_noalloc: tt_unmask_step with its vocabulary partials in a
+// static device array instead of a caller workspace.
+// ---------------------------------------------------------------------------
+
+// Every GPU the library runs on holds its own copy of this array until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: only the address hipGetSymbolAddress returns for the current device
+// is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[TT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`, looked up once per device (with
+// that device current) and kept.
+tt_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return TT_ENODEV;
+  }
+  if (dev >= kMaxDevices) return TT_EUNSUPPORTED;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+        (void)hipGetLastError();
+        return TT_EHIP;
+      }
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return TT_OK;
+}
+
+}  // namespace
+
+TT_EXPORT tt_status tt_unmask_step_noalloc(const float* logits, const uint8_t* mask_state, int k,
+                                           int32_t* tokens_out, uint8_t* mask_out, int batch,
+                                           int block_len, int vocab, float* conf_out,
+                                           int32_t* pred_out, hipStream_t stream) {
+  tt_select sel{TT_SELECT_TOP_K, k, 0.0f, 1, 1, 1};
+  UnmaskParams p{};
+  tt_status st = set_select(&sel, &p);
+  if (st != TT_OK) return st;
+  UnmaskPlan plan;
+  st = plan_unmask(batch, block_len, vocab, &plan);
+  if (st != TT_OK || plan.empty) return st;
+  if (plan.ws_bytes > (size_t)TT_NOALLOC_SCRATCH_BYTES) return TT_EUNSUPPORTED;
+  if (!logits || !mask_state || !tokens_out || !mask_out) return TT_EINVAL;
+  st = device_present();
+  if (st != TT_OK) return st;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != TT_OK) return st;
+  // Nothing in the array needs clearing: the vocabulary pass writes the
+  // partial of every (masked position, chunk) before the commit reads it, and
+  // the slots of unmasked positions are read and ignored.
+  return unmask_run(logits, mask_state, &sel, tokens_out, mask_out, batch, block_len, vocab,
+                    conf_out, pred_out, ws, (size_t)TT_NOALLOC_SCRATCH_BYTES, stream, true);
+}

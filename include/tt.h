@@ -309,6 +309,24 @@ tt_status tt_unmask_commit_ex(const uint8_t* mask_state, const tt_select* select
                               int vocab, float* conf_out, int32_t* pred_out,
                               const void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): exactly
+ * tt_unmask_step, with the same arguments, outputs and guarantees, except that
+ * its vocabulary partials live in a static device array of
+ * TT_NOALLOC_SCRATCH_BYTES owned by the library (one per GPU, held until the
+ * process ends) instead of a caller workspace.  The call allocates and frees
+ * nothing.  Sizes whose workspace (tt_unmask_workspace_bytes) would exceed
+ * TT_NOALLOC_SCRATCH_BYTES return TT_EUNSUPPORTED (8 MiB: e.g. 16384
+ * positions of a 131072-word vocabulary).  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (other streams, other
+ * threads) race and give undefined results; calls ordered on one stream are
+ * safe.  The array needs no clearing between calls. */
+#define TT_NOALLOC_SCRATCH_BYTES (8u << 20)
+tt_status tt_unmask_step_noalloc(const float* logits, const uint8_t* mask_state, int k,
+                                 int32_t* tokens_out, uint8_t* mask_out, int batch, int block_len,
+                                 int vocab, float* conf_out, int32_t* pred_out,
+                                 hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Fused LM head + unmask: TwoTower paper §2.2 "Sampling", Algorithm 2.       */
 /* ------------------------------------------------------------------------ */

@@ -324,3 +324,34 @@ def test_attn_rejects_misaligned_workspace_and_lengths():
 def test_lmhead_rejects_misaligned(kw):
     assert lmhead_call(**kw) == B.TT_EINVAL
 
+
+def noalloc_call(**kw):
+    a = dict(logits=FAKE, mask=FAKE, k=4, tokens=FAKE, mask_out=FAKE, batch=1, L=16, V=1000,
+             conf=None, pred=None, stream=None)
+    a.update(kw)
+    return tt.lib().tt_unmask_step_noalloc(a["logits"], a["mask"], a["k"], a["tokens"],
+                                           a["mask_out"], a["batch"], a["L"], a["V"], a["conf"],
+                                           a["pred"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(logits=None), B.TT_EINVAL), (dict(mask=None), B.TT_EINVAL),
+    (dict(tokens=None), B.TT_EINVAL), (dict(mask_out=None), B.TT_EINVAL),
+    (dict(k=-1), B.TT_EINVAL), (dict(V=0), B.TT_EINVAL), (dict(L=1025), B.TT_EUNSUPPORTED),
+    # partials beyond the static scratch: 64 x 1024 positions x 32 chunks x 16 B = 32 MiB
+    (dict(batch=64, L=1024, V=131072), B.TT_EUNSUPPORTED),
+    (dict(batch=0, logits=None), B.TT_OK),
+])
+def test_noalloc_validates_before_any_device_call(kw, status):
+    assert noalloc_call(**kw) == status
+
+
+def test_noalloc_scratch_limit_matches_workspace_query():
+    # The largest calls that fit: the workspace query's bytes <= 8 MiB.
+    assert tt.unmask_workspace_bytes(128, 128, 131072) == B.NOALLOC_SCRATCH_BYTES
+    assert noalloc_call(batch=129, L=128, V=131072) == B.TT_EUNSUPPORTED
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a GPU")
+def test_noalloc_without_device_reports_enodev():
+    assert noalloc_call() == B.TT_ENODEV
