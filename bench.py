@@ -70,6 +70,8 @@ def parse_args():
     ap.add_argument("--lmhead-only", action="store_true",
                     help="instead of the step: only the fused LM head workloads of the suite "
                          "(256 and 4096 masked rows), for kernel traces")
+    ap.add_argument("--only", default="",
+                    help="--suite sections to run, comma-separated: " + ", ".join(SUITE_SECTIONS))
     ap.add_argument("--kernel-reps", type=int, default=200,
                     help="back-to-back launches timed for the per-kernel roofline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -201,26 +203,49 @@ def _roof(bytes_, flops):
     return max(t_hbm, t_mfma), ("hbm" if t_hbm >= t_mfma else "mfma")
 
 
+SUITE_SECTIONS = ("probes", "attention", "gen8k_sweep", "varlen", "multiblock", "unmask",
+                  "selection", "trace8k", "layers6", "crossover", "lmhead")
+
+
 def suite(args):
-    """Supplementary measurements, one JSON line each (not the headline)."""
+    """Supplementary measurements, one JSON line each (not the headline).
+
+    Sections (``--only a,b``; default all): roof probes (what this chip
+    sustains: HBM streaming read, back-to-back bf16 MFMA), attention at every
+    configuration and the prefix-bound shapes, the 8K-generation prefix sweep,
+    per-sequence prefixes, the multi-block pass, the unmask at every
+    configuration over every step of a block, the selection rules, the
+    8K-token generation trace (32 blocks of 256), the step with six attention
+    layers, the MFMA / wavefront-shuffle crossover, and the fused LM head.
+    Every line carries its fraction of the datasheet roof and, once the probes
+    have run, of the measured roof.  Inputs are drawn on the device
+    (N(0,1) bf16 Q/K/V, N(0,3) fp32 logits): timings do not depend on values."""
+    import ctypes
+
     import torch
 
     sys.path.insert(0, ROOT)
     import denoiser_attention_amd as tt
     from denoiser_attention_amd import synth
 
+    only = set(SUITE_SECTIONS if not args.only else args.only.split(","))
+    unknown = only - set(SUITE_SECTIONS)
+    if unknown:
+        raise SystemExit(f"bench.py: unknown suite sections {sorted(unknown)}")
+    if args.attn_only:
+        only = {"attn_only"}
+    if args.lmhead_only:
+        only = {"lmhead"}
+
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(dev)
     reps = max(10, args.kernel_reps // 4)
-
-    def up(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    measured = {}    # measured roofs: "hbm" GB/s, "mfma" TFLOP/s
 
     def time_calls(fns, n=reps):
-        """Average us per call over back-to-back calls (rotating fns), HIP events,
-        after at least 50 ms of untimed calls (the clocks ramp up under load)."""
+        """Average us per call over back-to-back calls (rotating fns), HIP events
+        on the launch stream, after at least 50 ms of untimed calls (the clocks
+        ramp up under load)."""
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
@@ -230,7 +255,7 @@ def suite(args):
                 for _ in range(8):
                     fns[i % len(fns)]()
                     i += 1
-                torch.cuda.synchronize()
+                stream.synchronize()
             e0.record(stream)
             for i in range(n):
                 fns[i % len(fns)]()
@@ -238,41 +263,352 @@ def suite(args):
         torch.cuda.synchronize()
         return 1e3 * e0.elapsed_time(e1) / n
 
-    def emit(name, us, bytes_, flops, **extra):
+    def fracs(us, bytes_, flops):
         roof_s, bound = _roof(bytes_, flops)
-        line = {"suite": name, "avg_us": us, "bound": bound, "roof_us": roof_s * 1e6,
-                "roof_frac": roof_s * 1e6 / us, "GBps": bytes_ / us / 1e3,
-                "TFLOPs": flops / us / 1e6}
+        out = {"bound": bound, "roof_us": roof_s * 1e6, "roof_frac": roof_s * 1e6 / us}
+        if measured:
+            t_m = max(bytes_ / (measured["hbm"] * 1e9), flops / (measured["mfma"] * 1e12))
+            out["measured_roof_us"] = t_m * 1e6
+            out["measured_roof_frac"] = t_m * 1e6 / us
+        return out
+
+    def emit(name, us, bytes_, flops, **extra):
+        line = {"suite": name, "avg_us": us}
+        line.update(fracs(us, bytes_, flops))
+        line.update({"GBps": bytes_ / us / 1e3, "TFLOPs": flops / us / 1e6})
         line.update(extra)
         print(json.dumps(line), flush=True)
 
-    def n_rotate(set_bytes):
+    def n_rotate(set_bytes, cap=48):
         # Enough independent input sets that one pass over them exceeds 1 GB
-        # (four times the Infinity Cache), as in the step benchmark.
-        return int(min(48, max(2, np.ceil(1.0e9 / set_bytes))))
+        # (four times the Infinity Cache).
+        return int(min(cap, max(2, np.ceil(1.0e9 / set_bytes))))
 
-    def attn_case(name, cfg, **kw):
-        B, Hq, Hkv, D, L = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_len
-        P = cfg.prefix_len if "prefix_len" not in kw else kw["prefix_len"]
-        n_sets = n_rotate(2 * (2 * B * Hq * L * D + 2 * B * Hkv * (P + L) * D))
+    def randn_bf16(*shape):
+        return torch.randn(*shape, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    def attn_bytes_flops(B, Hq, Hkv, D, L, P, s=2):
+        return (s * (2 * B * Hq * L * D + 2 * B * Hkv * (P + L) * D), 4 * B * Hq * L * (P + L) * D)
+
+    def attn_case(name, B, Hq, Hkv, D, L, P, scale=None, path="auto", extra=None, n=None):
+        scale = 1.0 / np.sqrt(D) if scale is None else scale
+        bytes_, flops = attn_bytes_flops(B, Hq, Hkv, D, L, P)
+        n_sets = n_rotate(bytes_)
         fns, keep = [], []
-        for r in range(n_sets):
-            inp = synth.attn_inputs(cfg, seed=0, step=r, **kw)
-            t = {n: up(inp[n]) for n in ("q", "k_ctx", "v_ctx", "k_blk", "v_blk")}
+        for _ in range(n_sets):
+            t = dict(q=randn_bf16(B, Hq, L, D), k_ctx=randn_bf16(B, Hkv, P, D),
+                     v_ctx=randn_bf16(B, Hkv, P, D), k_blk=randn_bf16(B, Hkv, L, D),
+                     v_blk=randn_bf16(B, Hkv, L, D))
             out = torch.empty_like(t["q"])
             with torch.cuda.stream(stream):
                 fns.append(tt.prepare_block_attn(t["q"], t["k_ctx"], t["v_ctx"], P, t["k_blk"],
-                                                 t["v_blk"], cfg.softmax_scale, out, stream=stream))
+                                                 t["v_blk"], scale, out, path=path, stream=stream))
             keep.append((t, out))
-        us = time_calls(fns)
-        s = 2
-        emit(name, us, s * (2 * B * Hq * L * D + 2 * B * Hkv * (P + L) * D),
-             4 * B * Hq * L * (P + L) * D, kind="attention", B=B, P=P, L=L, Hq=Hq, Hkv=Hkv, D=D,
-             input_sets=n_sets)
+        torch.cuda.synchronize()
+        us = time_calls(fns, n=n or reps)
+        ex = dict(kind="attention", B=B, P=P, L=L, Hq=Hq, Hkv=Hkv, D=D, path=path,
+                  workspace_bytes=tt.attn_workspace_bytes(B, P, L, Hq, Hkv, D, torch.bfloat16,
+                                                          path=path),
+                  input_sets=n_sets)
+        ex.update(extra or {})
+        emit(name, us, bytes_, flops, **ex)
         del keep, fns
+        return us
 
-    def lmhead_section():
-        # Fused LM head + unmask vs the library GEMM + this unmask.
+    def cfg_attn(name, **kw):
+        c = synth.get_config(name, **kw)
+        return attn_case(f"attn {name} P={c.prefix_len}", c.batch, c.n_q_heads, c.n_kv_heads,
+                         c.head_dim, c.block_len, c.prefix_len)
+
+    # ---- roof probes ----------------------------------------------------------
+    if "probes" in only:
+        probe = ctypes.CDLL(os.path.join(ROOT, "denoiser_attention_amd", "libtt_probes.so"))
+        probe.tt_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        probe.tt_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_void_p, ctypes.c_void_p]
+        probe.tt_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+        probe.tt_probe_mfma_bf16_flops.restype = ctypes.c_double
+        sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+        nbytes = 1 << 30
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(2)]
+        torch.cuda.synchronize()
+
+        def hbm_call(b):
+            def f():
+                if probe.tt_probe_hbm_read(b.data_ptr(), nbytes, sink.data_ptr(),
+                                           stream.cuda_stream) != 0:
+                    raise RuntimeError("tt_probe_hbm_read failed")
+            return f
+        us = time_calls([hbm_call(b) for b in bufs], n=40)
+        measured_hbm = nbytes / us / 1e3
+        emit("probe hbm streaming read 1 GiB (16 B non-temporal loads, 16 KB per workgroup)", us,
+             nbytes, 0, kind="probe", measured_GBps=measured_hbm)
+        del bufs
+        n_wg, iters = 512, 4096
+        flops = probe.tt_probe_mfma_bf16_flops(n_wg, iters)
+        rates = {}
+        for rnd in (0, 1):
+            def mfma_call(rnd=rnd):
+                if probe.tt_probe_mfma_bf16(n_wg, iters, rnd, sink.data_ptr(),
+                                            stream.cuda_stream) != 0:
+                    raise RuntimeError("tt_probe_mfma_bf16 failed")
+            us = time_calls([mfma_call], n=40)
+            rates[rnd] = flops / us / 1e6
+            kind = "random operands" if rnd else "low-entropy operands"
+            emit(f"probe bf16 mfma 32x32x16 {kind}, {n_wg} workgroups x 4 waves x {iters} x 4 "
+                 "chains", us, 0, flops, kind="probe", measured_TFLOPs=rates[rnd])
+        # The measured MFMA roof: random operands, as attention tiles are.
+        measured_mfma = rates[1]
+        measured.update(hbm=measured_hbm, mfma=measured_mfma)
+
+    if "attn_only" in only:
+        kw = {} if args.prefix_len is None else {"prefix_len": args.prefix_len}
+        cfg_attn(args.config, **kw)
+        return
+
+    # ---- attention at every configuration and the prefix-bound shapes ---------
+    if "attention" in only:
+        for name, kw in (("decode_b8_p2048_l32", {}), ("block256_b16_p1024", {}),
+                         ("gen8k_b4_l256", dict(prefix_len=512)),
+                         ("gen8k_b4_l256", dict(prefix_len=8192)),
+                         ("gen8k_b4_l256", dict(prefix_len=16128)),
+                         ("highbatch_b64_p4096_l64", {}), ("decode_l16", {}), ("decode_l1", {}),
+                         ("decode_b64_p4096_l1", {}), ("decode_b128_p2048_l1", {})):
+            cfg_attn(name, **kw)
+
+    if "gen8k_sweep" in only:
+        for P in synth.GEN8K_SWEEP:
+            cfg_attn("gen8k_b4_l256", prefix_len=P)
+
+    # ---- per-sequence prefix lengths ---------------------------------------------
+    if "varlen" in only:
+        cfg = synth.get_config("decode_b8_p2048_l32")
+        inp = synth.varlen_inputs(cfg, seed=0, max_prefix_len=2048)
+        t = {n: torch.from_numpy(inp[n].view(np.int16)).to(dev).view(torch.bfloat16)
+             for n in ("q", "k_ctx", "v_ctx", "k_blk", "v_blk")}
+        lens = torch.from_numpy(inp["prefix_lens"]).to(dev)
+        out = torch.empty_like(t["q"])
+        fn = lambda: tt.block_attn_varlen(t["q"], t["k_ctx"], t["v_ctx"], lens, 2048, t["k_blk"],
+                                          t["v_blk"], cfg.softmax_scale, out=out, stream=stream)
+        us = time_calls([fn])
+        Ps = inp["prefix_lens"].astype(np.int64)
+        B, Hq, Hkv, D, L = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_len
+        emit("attn varlen decode_b8 lens=" + ",".join(map(str, Ps.tolist())), us,
+             2 * (2 * B * Hq * L * D + 2 * Hkv * int((Ps + L).sum()) * D),
+             4 * Hq * L * int((Ps + L).sum()) * D, kind="attention varlen")
+        del t, out
+
+    # ---- training-style pass over all noisy blocks ------------------------------
+    if "multiblock" in only:
+        Hq, Hkv, D, S = 32, 2, 128, 256
+        for nb in (8, 32):
+            T = nb * S
+            q, kn, vn = randn_bf16(1, Hq, T, D), randn_bf16(1, Hkv, T, D), randn_bf16(1, Hkv, T, D)
+            kc, vc = randn_bf16(1, Hkv, T, D), randn_bf16(1, Hkv, T, D)
+            out = torch.empty_like(q)
+            fn = lambda: tt.block_attn_multiblock(q, kc, vc, kn, vn, S, 1.0 / np.sqrt(D), out=out,
+                                                  stream=stream)
+            us = time_calls([fn], n=max(5, reps // 4))
+            keys = sum(j * S + S for j in range(nb))
+            emit(f"attn multiblock {nb}x256 batch=1", us,
+                 2 * (2 * Hq * nb * S * D + 2 * Hkv * (nb * S + (nb - 1) * S) * D),
+                 4 * Hq * S * keys * D, kind="attention multiblock")
+            del q, kn, vn, kc, vc, out
+
+    # ---- unmask at every configuration over every step of a block ---------------
+    def unmask_steps(name, B, L, V, k, T, n_sets):
+        """Step r of T: the reduce and commit over the masked set the kernels
+        themselves left after steps 1..r-1 (top-k, k per step)."""
+        xs = [torch.randn(B, L, V, device=dev) * 3.0 for _ in range(n_sets)]
+        mask = torch.ones((B, L), dtype=torch.uint8, device=dev)
+        tok = torch.zeros((B, L), dtype=torch.int32, device=dev)
+        ws = torch.empty(tt.unmask_workspace_bytes(B, L, V), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        total_us = 0.0
+        for r in range(1, T + 1):
+            n_masked = int(mask.sum().item())
+            mo = torch.empty_like(mask)
+            with torch.cuda.stream(stream):
+                reds = [tt.prepare_unmask_reduce(x, mask, ws, stream=stream) for x in xs]
+                com = tt.prepare_unmask_commit(mask, k, tok, mo, V, ws, stream=stream)
+            torch.cuda.synchronize()
+            us_r = time_calls(reds)
+            us_c = time_calls([com])
+            total_us += us_r + us_c
+            emit(f"unmask {name} step {r}/{T} reduce", us_r, n_masked * V * 4 + B * L, 0,
+                 kind="vocabulary pass", masked=n_masked, commit_us=us_c, input_sets=n_sets)
+            with torch.cuda.stream(stream):
+                reds[0]()
+                com()
+            torch.cuda.synchronize()
+            mask = mo
+        return total_us
+
+    if "unmask" in only:
+        for name in ("decode_b8_p2048_l32", "block256_b16_p1024", "gen8k_b4_l256",
+                     "highbatch_b64_p4096_l64"):
+            c = synth.get_config(name)
+            n_sets = 2 if c.batch * c.block_len * c.vocab * 4 > 4.0e8 else 8
+            tot = unmask_steps(name, c.batch, c.block_len, c.vocab, c.k, c.steps, n_sets)
+            print(json.dumps({"suite": f"unmask {name} whole block ({c.steps} steps)",
+                              "avg_us": tot, "kind": "unmask block",
+                              "committed_tokens": c.batch * c.block_len}), flush=True)
+
+    # ---- selection rules (decode workload, all positions masked) ---------------
+    if "selection" in only:
+        cfg = synth.get_config("decode_b8_p2048_l32")
+        B, L, V = cfg.batch, cfg.block_len, cfg.vocab
+        x = torch.randn(B, L, V, device=dev) * 3.0
+        mask = torch.ones((B, L), dtype=torch.uint8, device=dev)
+        tok = torch.zeros((B, L), dtype=torch.int32, device=dev)
+        mo = torch.empty_like(mask)
+        ws = torch.empty(tt.unmask_workspace_bytes(B, L, V), dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(stream):
+            tt.prepare_unmask_reduce(x, mask, ws, stream=stream)()
+        for mode, params in (("top_k", dict(k=8)), ("threshold", dict(gamma=0.8, steps_left=4)),
+                             ("schedule", dict(step=1, n_steps=4)), ("leftmost", dict(k=1))):
+            with torch.cuda.stream(stream):
+                c = tt.prepare_unmask_commit_ex(mask, tt.select_rule(mode, **params), tok, mo, V,
+                                                ws, stream=stream)
+            emit(f"unmask commit {mode} decode_b8", time_calls([c]), B * L * 16 * 16 + 2 * B * L,
+                 0, kind="selection")
+        del x
+
+    # ---- 8K tokens generated as 32 blocks of 256 ---------------------------------
+    if "trace8k" in only:
+        cfg = synth.get_config("gen8k_b4_l256")
+        B, L, Hq, Hkv, D, V, k = (cfg.batch, cfg.block_len, cfg.n_q_heads, cfg.n_kv_heads,
+                                  cfg.head_dim, cfg.vocab, cfg.k)
+        prompt, n_blocks, T = 8192, 32, cfg.steps
+        cap = prompt + L * n_blocks
+        kc, vc = randn_bf16(B, Hkv, cap, D), randn_bf16(B, Hkv, cap, D)
+        qs = [randn_bf16(B, Hq, L, D) for _ in range(2)]
+        kbs = [randn_bf16(B, Hkv, L, D) for _ in range(2)]
+        vbs = [randn_bf16(B, Hkv, L, D) for _ in range(2)]
+        xs = [torch.randn(B, L, V, device=dev) * 3.0 for _ in range(2)]
+        out = torch.empty_like(qs[0])
+        tok = torch.zeros((B, L), dtype=torch.int32, device=dev)
+        masks = [torch.empty((B, L), dtype=torch.uint8, device=dev) for _ in range(T + 1)]
+        ws_u = torch.empty(tt.unmask_workspace_bytes(B, L, V), dtype=torch.uint8, device=dev)
+        ws_a = torch.empty(max(1, max(tt.attn_workspace_bytes(B, prompt + L * b, L, Hq, Hkv, D,
+                                                              torch.bfloat16)
+                                      for b in range(n_blocks))), dtype=torch.uint8, device=dev)
+        scale = 1.0 / np.sqrt(D)
+
+        # Every call validated once up front (one prepared call per block's
+        # prefix length, per step's masks and per logits set); the trace then
+        # costs one ctypes call per launch on the host.
+        with torch.cuda.stream(stream):
+            attn_calls = [[tt.prepare_block_attn(qs[j], kc, vc, prompt + L * b, kbs[j], vbs[j],
+                                                 scale, out, workspace=ws_a, stream=stream)
+                           for j in range(2)] for b in range(n_blocks)]
+            red_calls = [[tt.prepare_unmask_reduce(xs[j], masks[r], ws_u, stream=stream)
+                          for j in range(2)] for r in range(T)]
+            com_calls = [tt.prepare_unmask_commit(masks[r], k, tok, masks[r + 1], V, ws_u,
+                                                  stream=stream) for r in range(T)]
+            reset = masks[0].fill_
+        torch.cuda.synchronize()
+
+        def trace(layers=1):
+            i = 0
+            for b in range(n_blocks):
+                reset(1)
+                for r in range(T):
+                    for _ in range(layers):
+                        attn_calls[b][i % 2]()
+                    red_calls[r][i % 2]()
+                    com_calls[r]()
+                    i += 1
+
+        roof_s = 0.0
+        roof_bytes = roof_flops = 0
+        n_masked = [L - k * r for r in range(T)]
+        for b in range(n_blocks):
+            P = prompt + L * b
+            ab, af = attn_bytes_flops(B, Hq, Hkv, D, L, P)
+            for r in range(T):
+                roof_s += _roof(ab, af)[0] + _roof(B * n_masked[r] * V * 4 + B * L, 0)[0]
+                roof_bytes += ab + B * n_masked[r] * V * 4 + B * L
+                roof_flops += af
+        for layers in (1, 6):
+            with torch.cuda.stream(stream):
+                trace(layers)      # warm
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                trace(layers)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            if layers == 1:
+                roof_l = roof_s
+            else:
+                roof_l = 0.0
+                for b in range(n_blocks):
+                    ab, af = attn_bytes_flops(B, Hq, Hkv, D, L, prompt + L * b)
+                    for r in range(T):
+                        roof_l += 6 * _roof(ab, af)[0] + _roof(B * n_masked[r] * V * 4, 0)[0]
+            tokens = B * L * n_blocks
+            print(json.dumps({
+                "suite": f"generation trace gen8k: {n_blocks} blocks of {L} after a {prompt}-token "
+                         f"prompt, {T} unmask steps of k={k} per block, {layers} attention "
+                         f"layer(s) per step",
+                "ms": ms, "committed_tokens": tokens, "committed_tokens_per_s": tokens / (ms * 1e-3),
+                "block_tokens_per_s": B * L * n_blocks * T / (ms * 1e-3),
+                "roof_ms": roof_l * 1e3, "roof_frac": roof_l * 1e3 / ms,
+                "kind": "generation trace"}), flush=True)
+        del kc, vc, xs
+
+    # ---- the step with six attention layers ----------------------------------------
+    if "layers6" in only:
+        for name in ("highbatch_b64_p4096_l64", "decode_b8_p2048_l32", "block256_b16_p1024"):
+            c = synth.get_config(name)
+            B, L, V, Hq, Hkv, D, P = (c.batch, c.block_len, c.vocab, c.n_q_heads, c.n_kv_heads,
+                                      c.head_dim, c.prefix_len)
+            layers = [dict(q=randn_bf16(B, Hq, L, D), kc=randn_bf16(B, Hkv, P, D),
+                           vc=randn_bf16(B, Hkv, P, D), kb=randn_bf16(B, Hkv, L, D),
+                           vb=randn_bf16(B, Hkv, L, D)) for _ in range(6)]
+            x = torch.randn(B, L, V, device=dev) * 3.0
+            mask = torch.ones((B, L), dtype=torch.uint8, device=dev)
+            mo = torch.empty_like(mask)
+            tok = torch.zeros((B, L), dtype=torch.int32, device=dev)
+            out = torch.empty_like(layers[0]["q"])
+            ws_a = torch.empty(max(1, tt.attn_workspace_bytes(B, P, L, Hq, Hkv, D, torch.bfloat16)),
+                               dtype=torch.uint8, device=dev)
+            ws_u = torch.empty(tt.unmask_workspace_bytes(B, L, V), dtype=torch.uint8, device=dev)
+            with torch.cuda.stream(stream):
+                calls = [tt.prepare_block_attn(l["q"], l["kc"], l["vc"], P, l["kb"], l["vb"],
+                                               c.softmax_scale, out, workspace=ws_a, stream=stream)
+                         for l in layers]
+                calls.append(tt.prepare_unmask_reduce(x, mask, ws_u, stream=stream))
+                calls.append(tt.prepare_unmask_commit(mask, c.k, tok, mo, V, ws_u, stream=stream))
+
+            def step6():
+                for f in calls:
+                    f()
+            us = time_calls([step6], n=max(10, reps // 2))
+            ab, af = attn_bytes_flops(B, Hq, Hkv, D, L, P)
+            ub = B * L * V * 4 + B * L
+            roof = 6 * _roof(ab, af)[0] + _roof(ub, 0)[0]
+            print(json.dumps({
+                "suite": f"step with 6 attention layers {name}", "avg_us": us,
+                "block_tokens_per_s": B * L / (us * 1e-6), "roof_us": roof * 1e6,
+                "roof_frac": roof * 1e6 / us, "kind": "step x6 layers"}), flush=True)
+            del layers, x
+
+    # ---- MFMA / wavefront-shuffle crossover (G*L packed rows per KV head) --------
+    if "crossover" in only:
+        B, Hkv, D, P = 64, 2, 128, 4096
+        for G, L in ((1, 1), (2, 1), (4, 1), (8, 1), (12, 1), (16, 1), (24, 1), (32, 1),
+                     (4, 4), (8, 2), (16, 2)):
+            for path in ("mfma", "shuffle"):
+                attn_case(f"crossover G*L={G * L} (G={G}, L={L}) B{B} P{P} {path}", B, G * Hkv, Hkv,
+                          D, L, P, path=path, extra=dict(kind="crossover", rows_per_kv_head=G * L))
+
+    # ---- fused LM head + unmask vs the library GEMM + this unmask ---------------
+    if "lmhead" in only:
         d = synth.LM_D_MODEL
         for name, B, L in (("decode_b8", 8, 32), ("block256_b16", 16, 256)):
             V = 131072
@@ -283,8 +619,8 @@ def suite(args):
             tok = torch.zeros((B, L), dtype=torch.int32, device=dev)
             mo = torch.empty_like(mask)
             with torch.cuda.stream(stream):
-                call = tt.prepare_lmhead_unmask_step(h, w, mask, tt.select_rule("top_k", k=8), tok, mo,
-                                                     stream=stream)
+                call = tt.prepare_lmhead_unmask_step(h, w, mask, tt.select_rule("top_k", k=8), tok,
+                                                     mo, stream=stream)
             us = time_calls([call], n=10)
             rows = B * L
             logits = torch.empty((rows, V), dtype=torch.float32, device=dev)
@@ -298,83 +634,6 @@ def suite(args):
             emit(f"lmhead+unmask {name} rows={rows} V={V} d={d}", us, V * d * 2 + rows * d * 2,
                  2.0 * rows * V * d, kind="fused LM head", unfused_library_gemm_us=us_u)
             del h, w, logits
-
-
-    if args.lmhead_only:
-        lmhead_section()
-        return
-
-    if args.attn_only:
-        kw = {} if args.prefix_len is None else {"prefix_len": args.prefix_len}
-        cfg = synth.get_config(args.config, **kw)
-        attn_case(f"attn {args.config} P={cfg.prefix_len}", cfg)
-        return
-
-    # Attention at every configuration (bf16) and the prefix-bound shapes.
-    for name, kw in (("decode_b8_p2048_l32", {}), ("block256_b16_p1024", {}),
-                     ("gen8k_b4_l256", dict(prefix_len=512)), ("gen8k_b4_l256", dict(prefix_len=8192)),
-                     ("gen8k_b4_l256", dict(prefix_len=16128)), ("highbatch_b64_p4096_l64", {}),
-                     ("decode_l16", {}), ("decode_l1", {}), ("decode_b64_p4096_l1", {}),
-                     ("decode_b128_p2048_l1", {})):
-        cfg = synth.get_config(name, **kw)
-        attn_case(f"attn {name} P={cfg.prefix_len}", cfg)
-
-    # Per-sequence prefix lengths (decode geometry, lengths mixed in [0, 2048]).
-    cfg = synth.get_config("decode_b8_p2048_l32")
-    inp = synth.varlen_inputs(cfg, seed=0, max_prefix_len=2048)
-    t = {n: up(inp[n]) for n in ("q", "k_ctx", "v_ctx", "k_blk", "v_blk")}
-    lens = torch.from_numpy(inp["prefix_lens"]).to(dev)
-    out = torch.empty_like(t["q"])
-    fn = lambda: tt.block_attn_varlen(t["q"], t["k_ctx"], t["v_ctx"], lens, 2048, t["k_blk"],
-                                      t["v_blk"], cfg.softmax_scale, out=out, stream=stream)
-    us = time_calls([fn])
-    Ps = inp["prefix_lens"].astype(np.int64)
-    B, Hq, Hkv, D, L = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_len
-    emit("attn varlen decode_b8 lens=" + ",".join(map(str, Ps.tolist())), us,
-         2 * (2 * B * Hq * L * D + 2 * Hkv * int((Ps + L).sum()) * D),
-         4 * Hq * L * int((Ps + L).sum()) * D, kind="attention varlen")
-    del t, out
-
-    # Training-style pass over all noisy blocks: 8 and 32 blocks of 256.
-    for nb, bsz in ((8, 1), (32, 1)):
-        cfg = synth.get_config("block256_b16_p1024")
-        mb = synth.multiblock_inputs(cfg, nb, 256, seed=0, batch=bsz)
-        t = {n: up(mb[n]) for n in ("q", "k_ctx", "v_ctx", "k_noisy", "v_noisy")}
-        out = torch.empty_like(t["q"])
-        fn = lambda: tt.block_attn_multiblock(t["q"], t["k_ctx"], t["v_ctx"], t["k_noisy"],
-                                              t["v_noisy"], 256, cfg.softmax_scale, out=out,
-                                              stream=stream)
-        us = time_calls([fn], n=max(5, reps // 4))
-        Hq, Hkv, D, S = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, 256
-        keys = sum(j * S + S for j in range(nb))        # visible keys per query row, summed over blocks
-        emit(f"attn multiblock {nb}x256 batch={bsz}", us,
-             2 * bsz * (2 * Hq * nb * S * D + 2 * Hkv * (nb * S + (nb - 1) * S) * D),
-             4 * bsz * Hq * S * keys * D, kind="attention multiblock")
-        del t, out
-
-    # Vocabulary pass and the selection rules (decode workload, all positions masked).
-    cfg = synth.get_config("decode_b8_p2048_l32")
-    B, L, V = cfg.batch, cfg.block_len, cfg.vocab
-    n_sets = n_rotate(B * L * V * 4)
-    xs = [up(synth.logits(cfg, seed=0, step=r)) for r in range(n_sets)]
-    mask = torch.ones((B, L), dtype=torch.uint8, device=dev)
-    tok = torch.zeros((B, L), dtype=torch.int32, device=dev)
-    mo = torch.empty_like(mask)
-    ws = torch.empty(tt.unmask_workspace_bytes(B, L, V), dtype=torch.uint8, device=dev)
-    with torch.cuda.stream(stream):
-        reds = [tt.prepare_unmask_reduce(x, mask, ws, stream=stream) for x in xs]
-        reds[0]()
-    emit("unmask reduce decode_b8", time_calls(reds), B * L * V * 4 + B * L, 0,
-         kind="vocabulary pass", input_sets=n_sets)
-    for mode, params in (("top_k", dict(k=8)), ("threshold", dict(gamma=0.8, steps_left=4)),
-                         ("schedule", dict(step=1, n_steps=4)), ("leftmost", dict(k=1))):
-        with torch.cuda.stream(stream):
-            c = tt.prepare_unmask_commit_ex(mask, tt.select_rule(mode, **params), tok, mo, V, ws,
-                                            stream=stream)
-        emit(f"unmask commit {mode} decode_b8", time_calls([c]), B * L * 16 * 16 + 2 * B * L, 0,
-             kind="selection")
-    del xs, reds
-    lmhead_section()
 
 
 def main():

@@ -1,4 +1,4 @@
-"""Build libtt.so in-tree with hipcc for gfx950.
+"""Build libtt.so (and the roof probes, libtt_probes.so) in-tree with hipcc for gfx950.
 
     python -m denoiser_attention_amd.build        # or: python denoiser_attention_amd/build.py
 
@@ -20,8 +20,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtt.so")
+PROBE_LIB = os.path.join(PKG, "libtt_probes.so")
 
 SOURCES = ["tt_api.cpp", "attn_mfma.hip", "attn_shuffle.hip", "unmask.hip", "lmhead.hip"]
+PROBE_SOURCES = ["probes.hip"]
 ARCH = "gfx950"
 
 COMMON = [
@@ -57,19 +59,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libtt.so.  Always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libtt.so and libtt_probes.so.  Always rebuilds."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
 
 

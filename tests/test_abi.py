@@ -355,3 +355,29 @@ def test_noalloc_scratch_limit_matches_workspace_query():
 @pytest.mark.skipif(torch.cuda.is_available(), reason="needs a host without a GPU")
 def test_noalloc_without_device_reports_enodev():
     assert noalloc_call() == B.TT_ENODEV
+
+
+PROBE_LIB = os.path.join(os.path.dirname(B.LIB_PATH), "libtt_probes.so")
+PROBE_HEADER = os.path.join(ROOT, "include", "tt_probes.h")
+
+
+@pytest.mark.skipif(not os.path.exists(PROBE_LIB), reason="libtt_probes.so not built")
+def test_probe_library_exports_and_validates():
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(tt_probe_[a-z0-9_]+)\s*\(", text)))
+    exported = os.popen(f"nm -D --defined-only {PROBE_LIB}").read()
+    assert sorted(set(re.findall(r"\bT (tt_\w+)", exported))) == names
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.tt_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    lib.tt_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    lib.tt_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.tt_probe_mfma_bf16_flops.restype = ctypes.c_double
+    assert lib.tt_probe_hbm_read(FAKE, 1000, FAKE, None) == 1        # not a multiple of 16 KB
+    assert lib.tt_probe_hbm_read(FAKE + 4, 1 << 14, FAKE, None) == 1  # misaligned
+    assert lib.tt_probe_hbm_read(None, 1 << 14, FAKE, None) == 1
+    assert lib.tt_probe_mfma_bf16(0, 16, 1, FAKE, None) == 1
+    assert lib.tt_probe_mfma_bf16(4, 0, 1, FAKE, None) == 1
+    assert lib.tt_probe_mfma_bf16(4, 10, 0, FAKE, None) == 1         # not a multiple of 4
+    assert lib.tt_probe_mfma_bf16_flops(512, 4096) == 512 * 16 * 4096 * 2 * 32 * 32 * 16
