@@ -84,7 +84,15 @@ tt_status plan_attn(long long B, int P, int L, int Hq, int Hkv, int D, tt_dtype 
     if (!shuffle_head_dim(D)) return TT_EUNSUPPORTED;
     plan->path = TT_ATTN_SHUFFLE;
   } else {
-    if (dtype == TT_BF16 && M >= 16 && mfma_head_dim(D)) {
+    // bf16 runs on the matrix cores at every packed-row count.  Forcing each
+    // kernel at B64 P4096 (2 KV heads, D 128, G*L packed rows per KV head from
+    // 1 to 32) measured the MFMA kernel 2.2x (G*L = 1) to 8x (G*L = 24)
+    // faster than the wavefront-shuffle kernel: the call streams the cache K/V
+    // either way, and the MFMA kernel's direct-to-LDS tile stream moves it at
+    // 5.1-5.6 TB/s, its mostly empty row tiles costing nothing there, where the
+    // shuffle kernel's per-key register loads reach 0.6-2.5 TB/s.  The shuffle
+    // kernel serves fp32 inputs and head_dim 256.
+    if (dtype == TT_BF16 && mfma_head_dim(D)) {
       plan->path = TT_ATTN_MFMA;
     } else if (shuffle_head_dim(D)) {
       plan->path = TT_ATTN_SHUFFLE;

@@ -61,9 +61,11 @@ typedef enum {
 
 typedef enum { TT_FP32 = 0, TT_BF16 = 1 } tt_dtype;
 
-/* Attention kernel family.  AUTO picks MFMA for bf16 inputs with at least 16
- * packed query rows per KV head (n_q_heads / n_kv_heads * block_len >= 16) and a
- * head_dim of 64 or 128, and the wavefront-shuffle kernel otherwise. */
+/* Attention kernel family.  AUTO picks MFMA for bf16 inputs with a head_dim of
+ * 64 or 128, at every number of packed query rows per KV head (measured faster
+ * than the wavefront-shuffle kernel from 1 to 32 such rows), and the
+ * wavefront-shuffle kernel for fp32 inputs and head_dim 256.  Either family
+ * can be forced through tt_attn_opts. */
 typedef enum { TT_ATTN_AUTO = 0, TT_ATTN_MFMA = 1, TT_ATTN_SHUFFLE = 2 } tt_attn_path;
 
 /* Optional tuning knobs of tt_block_attn_ex.  kv_splits = 0 lets the library

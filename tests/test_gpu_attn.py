@@ -36,7 +36,7 @@ def test_tiny_fp32_splits_and_padding(splits):
 SHAPES = [
     (2, 8, 2, 37, 150, 160, 128),    # M=148 (2 tiles, ragged), 187 keys (ragged)
     (1, 16, 1, 16, 64, 64, 128),     # M=256 exactly 2 tiles, 80 keys
-    (3, 4, 4, 5, 0, 0, 128),         # no prefix, G=1: M=5 -> shuffle under auto
+    (3, 4, 4, 5, 0, 0, 128),         # no prefix, G=1: M=5 (MFMA under auto)
     (2, 32, 2, 1, 300, 300, 128),    # single-token block, M=16 (MFMA eligible)
     (1, 8, 1, 33, 1, 1, 64),         # D=64, one prefix row
     (2, 6, 3, 20, 96, 96, 64),       # D=64, G=2, M=40

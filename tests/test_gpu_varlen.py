@@ -53,7 +53,7 @@ VARLEN_SHAPES = [
     (5, 8, 2, 37, 150, 160, 128),
     (4, 6, 3, 20, 96, 96, 64),
     (3, 32, 2, 1, 300, 300, 128),
-    (6, 4, 4, 5, 40, 45, 128),      # G*L = 5: shuffle kernel under auto
+    (6, 4, 4, 5, 40, 45, 128),      # G*L = 5 (MFMA under auto)
 ]
 
 
@@ -160,7 +160,7 @@ MB_SHAPES = [
     (2, 8, 2, 4, 16, 128),
     (2, 6, 3, 3, 37, 64),     # block size not a multiple of the key tile
     (1, 16, 2, 1, 40, 128),   # one block: no context row visible
-    (3, 4, 4, 5, 3, 128),     # G*S = 3: shuffle kernel under auto
+    (3, 4, 4, 5, 3, 128),     # G*S = 3 (MFMA under auto)
 ]
 
 
