@@ -256,26 +256,21 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     koff[i] = r * L::ROWB + ((q ^ L::fk(r)) << 4);
     voff[i] = r * L::ROWB + ((q ^ L::fv(r)) << 4);
   }
-  auto issue = [&](int t, int slot) {
+  auto issue = [&](int t, auto slot) {
     const uint32_t kst = smem_u32 + slot * L::STAGE_B;
     const uint32_t vst = kst + L::TILE_B;
     const int key0 = t * BN;
-    const char *kbase, *vbase;
-    bool uniform = true;
-    if (key0 + BN <= P) {
-      kbase = kc + (size_t)key0 * L::ROWB;
-      vbase = vc + (size_t)key0 * L::ROWB;
-    } else if (key0 >= P && key0 + BN <= n_keys) {
-      kbase = kb + (size_t)(key0 - P) * L::ROWB;
-      vbase = vb + (size_t)(key0 - P) * L::ROWB;
-    } else {
-      uniform = false;
-      kbase = vbase = nullptr;
-    }
+    const bool in_prefix = key0 + BN <= P;
+    const bool in_block = key0 >= P && key0 + BN <= n_keys;
+    if (__builtin_expect(in_prefix || in_block, 1)) {
+      // A tile wholly in the cache or wholly in the block (every tile but
+      // the one straddling the two and a ragged last one): one uniform base,
+      // chosen without a branch.
+      const char* kbase = in_prefix ? kc + (size_t)key0 * L::ROWB : kb + (size_t)(key0 - P) * L::ROWB;
+      const char* vbase = in_prefix ? vc + (size_t)key0 * L::ROWB : vb + (size_t)(key0 - P) * L::ROWB;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const uint32_t wofs = (i * NT + wave * 64) * 16;   // wave-uniform destination
-      if (uniform) {
+      for (int i = 0; i < LOADS; ++i) {
+        const uint32_t wofs = (i * NT + wave * 64) * 16;   // wave-uniform destination
         if constexpr (NT_LOADS) {
           dma16_s_nt(kbase, koff[i], kst + wofs);
           dma16_s_nt(vbase, voff[i], vst + wofs);
@@ -283,7 +278,11 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
           dma16_s(kbase, koff[i], kst + wofs);
           dma16_s(vbase, voff[i], vst + wofs);
         }
-      } else {
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const uint32_t wofs = (i * NT + wave * 64) * 16;
         const int j = min(key0 + rrow[i], n_keys - 1);
         const size_t rel = (size_t)rrow[i] * L::ROWB;
         const char* krow = j < P ? kc + (size_t)j * L::ROWB : kb + (size_t)(j - P) * L::ROWB;
@@ -369,7 +368,7 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
       mx[rb] = pair_max(mraw * c);
       grow = grow || mx[rb] > m_run[rb] + kLazyRescale;
     }
-    if (__any(grow)) {
+    if (__builtin_expect(__any(grow), 0)) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const float m_new = fmaxf(m_run[rb], mx[rb]);
@@ -466,6 +465,15 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     barrier();
     if (i + NS - 2 < cnt) issue(t_begin + i + NS - 2, slot_of(i + NS - 2));
   };
+  // The same where the caller guarantees that tile i + NS - 2 exists for
+  // this group (so NS - 3 tiles are still in flight behind tile i), with the
+  // refilled slot a compile-time constant: no branch and no runtime wait
+  // count in the steady state.
+  auto advance_steady = [&](int i, auto slot) {
+    wait_vmcnt<2 * LOADS * (NS - 3)>();
+    barrier();
+    issue(t_begin + i + NS - 2, slot);
+  };
   // Tile i (in ring slot `slot`): softmax and P.V, with the scores of tile
   // i+1 when DO_QK.  `slot` is an int or, in the loop unrolled by the ring
   // depth, a compile-time constant, so that the slot offsets fold into the
@@ -516,14 +524,17 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   if constexpr (NS == 4) {
     // Unrolled by the ring depth: i stays a multiple of 4, so tile i + j
     // lives in slot j.
-    for (; i + 5 < nit; i += 4) {
-      advance(i + 1);
+    // i + 7 < nit: tiles up to i + 6 exist for both key groups (group 0 has
+    // at least nit - 1 tiles), so every refill of this loop is unconditional.
+    static_assert(NS == 4, "the steady-state slots below assume a 4-deep ring");
+    for (; i + 7 < nit; i += 4) {
+      advance_steady(i + 1, std::integral_constant<int, 3>{});
       step(yes, no, i, s_a, s_b, std::integral_constant<int, 0>{});
-      advance(i + 2);
+      advance_steady(i + 2, std::integral_constant<int, 0>{});
       step(yes, no, i + 1, s_b, s_a, std::integral_constant<int, 1>{});
-      advance(i + 3);
+      advance_steady(i + 3, std::integral_constant<int, 1>{});
       step(yes, no, i + 2, s_a, s_b, std::integral_constant<int, 2>{});
-      advance(i + 4);
+      advance_steady(i + 4, std::integral_constant<int, 2>{});
       step(yes, no, i + 3, s_b, s_a, std::integral_constant<int, 3>{});
     }
   }
