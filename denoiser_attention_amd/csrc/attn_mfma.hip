@@ -337,6 +337,26 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     }
   };
 
+  // c * the row maximum of the scores most recently computed (both lanes of a
+  // row hold the same value).  It is formed while the matrix cores run the
+  // previous tile's P.V, so the next step starts from it.
+  float mx_pend[RB];
+  auto tile_max = [&](auto tail_tag, const Scores& sc, int t) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const int key0 = t * BN;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float mraw = POS_SCALE ? -INFINITY : INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ok = !TAIL || key0 + 8 * (r >> 2) + 4 * hh + (r & 3) < n_keys;
+        const float v = ok ? sc[rb][r] : (POS_SCALE ? -INFINITY : INFINITY);
+        mraw = POS_SCALE ? fmaxf(mraw, v) : fminf(mraw, v);
+      }
+      mx_pend[rb] = pair_max(mraw * c);
+    }
+  };
+
   // Online softmax of tile t's scores `sacc`, with the scores of the next
   // tile (K fragments kf, when DO_QK) computed in between: one MFMA of the
   // next tile's chain per slice of this tile's exponentials, so that the
@@ -359,13 +379,7 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     bool grow = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float mraw = POS_SCALE ? -INFINITY : INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float v = valid(r) ? sacc[rb][r] : (POS_SCALE ? -INFINITY : INFINITY);
-        mraw = POS_SCALE ? fmaxf(mraw, v) : fminf(mraw, v);
-      }
-      mx[rb] = pair_max(mraw * c);
+      mx[rb] = mx_pend[rb];   // tile t's row maximum, formed during the previous P.V
       grow = grow || mx[rb] > m_run[rb] + kLazyRescale;
     }
     if (__builtin_expect(__any(grow), 0)) {
@@ -422,7 +436,9 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // fragment shared by the row blocks.  Element j of the V^T operand of k-step
   // ks is key 16*ks + (j < 4 ? 4*hh + j : 8 + 4*hh + j - 4): the first
   // transposing read covers j < 4, the second (8 rows further) j >= 4.
-  auto finish_pv = [&](const bf16x8 (&pf)[RB][2], const float (&tsum)[RB], int slot) {
+  // `mid` runs between the first and the second half of the P.V MFMAs (the
+  // next tile's row maximum: VALU work for the matrix cores' shadow).
+  auto finish_pv = [&](const bf16x8 (&pf)[RB][2], const float (&tsum)[RB], int slot, auto mid) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) l_run[rb] += tsum[rb];
     const char* Vs = smem + slot * L::STAGE_B + L::TILE_B;
@@ -443,6 +459,7 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
         for (int rb = 0; rb < RB; ++rb)
           oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[rb][ks], oacc[rb][db], 0, 0, 0);
       }
+      if (db == L::DB / 2 - 1) mid();
     }
     if (KG == 1) __builtin_amdgcn_s_setprio(0);
   };
@@ -478,8 +495,8 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // i+1 when DO_QK.  `slot` is an int or, in the loop unrolled by the ring
   // depth, a compile-time constant, so that the slot offsets fold into the
   // LDS reads' immediate offsets.
-  auto step = [&](auto do_qk_tag, auto tail_tag, int i, const Scores& s_in, Scores& s_out,
-                  auto slot) {
+  auto step = [&](auto do_qk_tag, auto tail_tag, auto next_tail_tag, int i, const Scores& s_in,
+                  Scores& s_out, auto slot) {
     constexpr bool DO_QK = decltype(do_qk_tag)::value;
     const int v_slot = slot;
     const int k_slot = (v_slot + 1) & (NS - 1);
@@ -493,7 +510,9 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     bf16x8 pf[RB][2];
     float tsum[RB];
     qk_softmax(do_qk_tag, tail_tag, s_in, t_begin + i, kf, Ks, pf, tsum, s_out);
-    finish_pv(pf, tsum, v_slot);
+    finish_pv(pf, tsum, v_slot, [&] {
+      if constexpr (DO_QK) tile_max(next_tail_tag, s_out, t_begin + i + 1);
+    });
   };
   const std::true_type yes{};
   const std::false_type no{};
@@ -517,6 +536,10 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) s_a[rb] = f32x16{};
   }
+  if ((t_begin + 1) * BN > n_keys)
+    tile_max(yes, s_a, t_begin);
+  else
+    tile_max(no, s_a, t_begin);
   // Steady state, unrolled by two so that the score registers alternate
   // instead of being copied: both groups have tiles i and i+1 (group 0 has at
   // least nit - 1 tiles).
@@ -529,34 +552,39 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     static_assert(NS == 4, "the steady-state slots below assume a 4-deep ring");
     for (; i + 7 < nit; i += 4) {
       advance_steady(i + 1, std::integral_constant<int, 3>{});
-      step(yes, no, i, s_a, s_b, std::integral_constant<int, 0>{});
+      step(yes, no, no, i, s_a, s_b, std::integral_constant<int, 0>{});
       advance_steady(i + 2, std::integral_constant<int, 0>{});
-      step(yes, no, i + 1, s_b, s_a, std::integral_constant<int, 1>{});
+      step(yes, no, no, i + 1, s_b, s_a, std::integral_constant<int, 1>{});
       advance_steady(i + 3, std::integral_constant<int, 1>{});
-      step(yes, no, i + 2, s_a, s_b, std::integral_constant<int, 2>{});
+      step(yes, no, no, i + 2, s_a, s_b, std::integral_constant<int, 2>{});
       advance_steady(i + 4, std::integral_constant<int, 2>{});
-      step(yes, no, i + 3, s_b, s_a, std::integral_constant<int, 3>{});
+      step(yes, no, no, i + 3, s_b, s_a, std::integral_constant<int, 3>{});
     }
   }
   for (; i + 3 < nit; i += 2) {
     advance(i + 1);
-    step(yes, no, i, s_a, s_b, slot_of(i));
+    step(yes, no, no, i, s_a, s_b, slot_of(i));
     advance(i + 2);
-    step(yes, no, i + 1, s_b, s_a, slot_of(i + 1));
+    step(yes, no, no, i + 1, s_b, s_a, slot_of(i + 1));
   }
   if (i + 2 < nit) {
     advance(i + 1);
-    step(yes, no, i, s_a, s_b, slot_of(i));
+    step(yes, no, no, i, s_a, s_b, slot_of(i));
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) s_a[rb] = s_b[rb];
     ++i;
   }
   if (nit >= 2) {   // tile nit-2; group 0 may lack tile nit-1
     advance(nit - 1);
-    if (nit - 1 < cnt)
-      step(yes, no, nit - 2, s_a, s_b, slot_of(nit - 2));
-    else
-      step(no, no, nit - 2, s_a, s_b, slot_of(nit - 2));
+    if (nit - 1 < cnt) {
+      // The next tile, nit-1, is the sequence's last when it runs past the end.
+      if (t_end * BN > n_keys)
+        step(yes, no, yes, nit - 2, s_a, s_b, slot_of(nit - 2));
+      else
+        step(yes, no, no, nit - 2, s_a, s_b, slot_of(nit - 2));
+    } else {
+      step(no, no, no, nit - 2, s_a, s_b, slot_of(nit - 2));
+    }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) s_a[rb] = s_b[rb];
   }
@@ -564,9 +592,9 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // always the group's tile nit-1.
   if (nit - 1 < cnt) {
     if (t_end * BN > n_keys)
-      step(no, yes, nit - 1, s_a, s_b, slot_of(nit - 1));
+      step(no, yes, no, nit - 1, s_a, s_b, slot_of(nit - 1));
     else
-      step(no, no, nit - 1, s_a, s_b, slot_of(nit - 1));
+      step(no, no, no, nit - 1, s_a, s_b, slot_of(nit - 1));
   }
 
   float l_tot[RB];
