@@ -9,7 +9,9 @@ the tt_* C entry points exported.  Object files go to _build/ at the repo root.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -21,6 +23,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtt.so")
 PROBE_LIB = os.path.join(PKG, "libtt_probes.so")
+# Per-kernel register, spill, scratch and LDS figures reported by the compiler
+# for the last build (read by the CPU tests that guard against spills).
+RESOURCES = os.path.join(BUILD, "kernel_resources.json")
 
 SOURCES = ["tt_api.cpp", "attn_mfma.hip", "attn_shuffle.hip", "unmask.hip", "lmhead.hip"]
 PROBE_SOURCES = ["probes.hip"]
@@ -31,7 +36,27 @@ COMMON = [
     # Keep hipcc from selecting packed-fp32 VALU instructions.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
+    # Per-kernel resource remarks (registers, spills, scratch, LDS, occupancy).
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+
+_REMARK = re.compile(r"remark:\s+(Function Name|[A-Za-z][A-Za-z /\[\]]*?): (\S+) \[-Rpass-analysis")
+_FIELDS = {"TotalSGPRs": "sgprs", "VGPRs": "vgprs", "AGPRs": "agprs",
+           "ScratchSize [bytes/lane]": "scratch_bytes", "Occupancy [waves/SIMD]": "waves_per_simd",
+           "SGPRs Spill": "sgpr_spill", "VGPRs Spill": "vgpr_spill",
+           "LDS Size [bytes/block]": "lds_bytes"}
+
+
+def parse_resources(text: str) -> dict:
+    """Kernel name -> resource figures, from the compiler's resource remarks."""
+    out, cur = {}, None
+    for m in _REMARK.finditer(text):
+        key, val = m.group(1).strip(), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None and key in _FIELDS:
+            cur[_FIELDS[key]] = int(val) if val.isdigit() else val
+    return out
 
 
 def hipcc() -> str:
@@ -41,7 +66,7 @@ def hipcc() -> str:
     return exe
 
 
-def _compile(src: str, verbose: bool) -> str:
+def _compile(src: str, verbose: bool):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
@@ -51,12 +76,15 @@ def _compile(src: str, verbose: bool) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so; drop that line.
     noise = "'-packed-fp32-ops' is not a recognized feature"
-    msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    lines = [l for l in (r.stdout + r.stderr).splitlines() if noise not in l]
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{msg}")
+        raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(lines))
+    resources = parse_resources("\n".join(lines))
+    # Everything but the resource remarks (and the source excerpts under them).
+    msg = "\n".join(l for l in lines if "kernel-resource-usage" not in l and not re.match(r"^\s+(\d+ \||\|)", l))
     if msg.strip() and verbose:
         print(msg, flush=True)
-    return obj
+    return obj, resources
 
 
 def _link(objs, out, verbose):
@@ -75,7 +103,11 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = SOURCES + PROBE_SOURCES
     with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
-        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+        done = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    objs = {s: o for s, (o, _) in done.items()}
+    resources = {s: res for s, (_, res) in done.items()}
+    with open(RESOURCES, "w") as f:
+        json.dump(resources, f, indent=1, sort_keys=True)
     _link([objs[s] for s in SOURCES], LIB, verbose)
     _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB

@@ -375,11 +375,14 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     // Accumulator register r holds key 8*(r/4) + 4*hh + r%4 of the tile.
     const int key0 = t * BN;
     auto valid = [&](int r) { return !TAIL || key0 + 8 * (r >> 2) + 4 * hh + (r & 3) < n_keys; };
+    // 64-row waves form the maximum here: holding it across the P.V of the
+    // previous tile makes their register allocation spill.
+    if constexpr (RB == 2) tile_max(tail_tag, sacc, t);
     float mx[RB];
     bool grow = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      mx[rb] = mx_pend[rb];   // tile t's row maximum, formed during the previous P.V
+      mx[rb] = mx_pend[rb];   // tile t's row maximum (32-row waves: formed during the previous P.V)
       grow = grow || mx[rb] > m_run[rb] + kLazyRescale;
     }
     if (__builtin_expect(__any(grow), 0)) {
@@ -511,7 +514,7 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     float tsum[RB];
     qk_softmax(do_qk_tag, tail_tag, s_in, t_begin + i, kf, Ks, pf, tsum, s_out);
     finish_pv(pf, tsum, v_slot, [&] {
-      if constexpr (DO_QK) tile_max(next_tail_tag, s_out, t_begin + i + 1);
+      if constexpr (DO_QK && RB == 1) tile_max(next_tail_tag, s_out, t_begin + i + 1);
     });
   };
   const std::true_type yes{};
@@ -536,10 +539,12 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) s_a[rb] = f32x16{};
   }
-  if ((t_begin + 1) * BN > n_keys)
-    tile_max(yes, s_a, t_begin);
-  else
-    tile_max(no, s_a, t_begin);
+  if constexpr (RB == 1) {
+    if ((t_begin + 1) * BN > n_keys)
+      tile_max(yes, s_a, t_begin);
+    else
+      tile_max(no, s_a, t_begin);
+  }
   // Steady state, unrolled by two so that the score registers alternate
   // instead of being copied: both groups have tiles i and i+1 (group 0 has at
   // least nit - 1 tiles).
@@ -578,7 +583,7 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     advance(nit - 1);
     if (nit - 1 < cnt) {
       // The next tile, nit-1, is the sequence's last when it runs past the end.
-      if (t_end * BN > n_keys)
+      if (RB == 1 && t_end * BN > n_keys)
         step(yes, no, yes, nit - 2, s_a, s_b, slot_of(nit - 2));
       else
         step(yes, no, no, nit - 2, s_a, s_b, slot_of(nit - 2));
