@@ -25,10 +25,13 @@
 //     accumulator layout each lane owns ONE query row and 16 of the tile's 32
 //     keys (the other 16 sit in lane ^ 32), so the softmax statistics are
 //     per lane plus one cross-half exchange.
-//   * Online softmax in base 2 with the scale folded into the exponent; the
-//     reference maximum is refreshed lazily (accumulators are rescaled only
-//     when a tile maximum exceeds it by more than 2^8, so unnormalised weights
-//     stay below 256; the final normalisation makes this exact).
+//   * Online softmax in base 2 with the scale folded into the exponent.  The
+//     reference maximum is the first tile's row maximum, refreshed lazily:
+//     only when some lane's share of a tile's weights sums past 2^8 (so some
+//     weight may exceed 256, or overflowed) are the accumulators rescaled to
+//     the tile's maximum and that tile's weights formed again.  Unnormalised
+//     weights stay at most 256 and the final normalisation makes this exact;
+//     the steady state needs no per-tile row maximum.
 //   * O^T += V^T P^T with the same MFMA: P (bf16) comes straight from the score
 //     accumulators; the V^T operand is read from the row-major V tile with the
 //     transposing LDS read ds_read_b64_tr_b16 (each 16-lane group turns a
@@ -61,7 +64,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int BM = kAttnMfmaBM;   // 128 packed query rows per workgroup
 constexpr int BN = kAttnMfmaBN;   // 32 keys per pipeline stage
-constexpr float kLazyRescale = 8.0f;  // log2 headroom before the max is refreshed
+constexpr float kLazyLimit = 256.0f;  // a lane's tile weight sum that triggers a rescale
 static_assert(BM == 32 * kWaves, "one 32-row MFMA tile per wave");
 static_assert(BN == 32, "the score tile is one 32x32 MFMA block");
 
@@ -337,9 +340,9 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     }
   };
 
-  // c * the row maximum of the scores most recently computed (both lanes of a
-  // row hold the same value).  It is formed while the matrix cores run the
-  // previous tile's P.V, so the next step starts from it.
+  // c * the row maximum of the scores `sc` of tile t (both lanes of a row hold
+  // the same value): the first tile's sets the reference maximum, later ones
+  // are formed only when a rescale is due.
   float mx_pend[RB];
   auto tile_max = [&](auto tail_tag, const Scores& sc, int t) {
     constexpr bool TAIL = decltype(tail_tag)::value;
@@ -360,13 +363,13 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // Online softmax of tile t's scores `sacc`, with the scores of the next
   // tile (K fragments kf, when DO_QK) computed in between: one MFMA of the
   // next tile's chain per slice of this tile's exponentials, so that the
-  // matrix core and the vector ALU work at the same time.  The reference max
-  // is refreshed lazily, before the exponentials: only when some row's tile
-  // max exceeds it by more than 2^8 (a uniform branch, rarely taken after the
-  // first tiles) are the accumulators rescaled.  Produces the bf16 P
-  // fragments and this lane's share of the tile's row sums.  The TAIL
-  // instantiation masks the keys past the end of the sequence (only the last
-  // tile can need it).
+  // matrix core and the vector ALU work at the same time.  The weights are
+  // formed against the current reference maximum; when some lane's share of
+  // a row's weights sums past kLazyLimit (a uniform branch, rarely taken
+  // after the first tile), the accumulators are rescaled to the tile's
+  // maximum and the weights formed again.  Produces the bf16 P fragments and
+  // this lane's share of the tile's row sums.  The TAIL instantiation masks
+  // the keys past the end of the sequence (only the last tile can need it).
   auto qk_softmax = [&](auto do_qk_tag, auto tail_tag, const Scores& sacc, int t,
                         const bf16x8 (&kf)[L::DS], const char* Ks, bf16x8 (&pf)[RB][2],
                         float (&tsum)[RB], Scores& snext) {
@@ -375,38 +378,24 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     // Accumulator register r holds key 8*(r/4) + 4*hh + r%4 of the tile.
     const int key0 = t * BN;
     auto valid = [&](int r) { return !TAIL || key0 + 8 * (r >> 2) + 4 * hh + (r & 3) < n_keys; };
-    // 64-row waves form the maximum here: holding it across the P.V of the
-    // previous tile makes their register allocation spill.
-    if constexpr (RB == 2) tile_max(tail_tag, sacc, t);
-    float mx[RB];
-    bool grow = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      mx[rb] = mx_pend[rb];   // tile t's row maximum (32-row waves: formed during the previous P.V)
-      grow = grow || mx[rb] > m_run[rb] + kLazyRescale;
-    }
-    if (__builtin_expect(__any(grow), 0)) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float m_new = fmaxf(m_run[rb], mx[rb]);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-        l_run[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < L::DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
-        m_run[rb] = m_new;
-      }
-    }
-
     // P = exp2(S*c - m) rounded to bf16, straight into MFMA B fragments; the
     // row sum adds exactly the bf16 weights that enter P.V (packed dot with 1).
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    auto weights = [&](int rb, int r) {
+      float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][r], c, -m_run[rb]));
+      float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][r + 1], c, -m_run[rb]));
+      if (!valid(r)) p0 = 0.0f;
+      if (!valid(r + 1)) p1 = 0.0f;
+      const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+      pf[rb][r >> 3][r & 7] = pk[0];
+      pf[rb][r >> 3][(r & 7) + 1] = pk[1];
+      tsum[rb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one2, tsum[rb], false);
+    };
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       snext[rb] = f32x16{};
       tsum[rb] = 0.0f;
     }
-    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
     constexpr int PER = 16 / L::DS;   // score registers per MFMA slice
 #pragma unroll
     for (int s = 0; s < L::DS; ++s) {
@@ -420,16 +409,27 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
       for (int rb = 0; rb < RB; ++rb) {
         if (DO_QK) snext[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ks_frag, qf[rb][s], snext[rb], 0, 0, 0);
 #pragma unroll
-        for (int r = s * PER; r < (s + 1) * PER; r += 2) {
-          float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][r], c, -m_run[rb]));
-          float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][r + 1], c, -m_run[rb]));
-          if (!valid(r)) p0 = 0.0f;
-          if (!valid(r + 1)) p1 = 0.0f;
-          const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-          pf[rb][r >> 3][r & 7] = pk[0];
-          pf[rb][r >> 3][(r & 7) + 1] = pk[1];
-          tsum[rb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one2, tsum[rb], false);
-        }
+        for (int r = s * PER; r < (s + 1) * PER; r += 2) weights(rb, r);
+      }
+    }
+    bool grow = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) grow = grow || tsum[rb] > kLazyLimit;
+    if (__builtin_expect(__any(grow), 0)) {
+      tile_max(tail_tag, sacc, t);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float m_new = fmaxf(m_run[rb], mx_pend[rb]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < L::DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
+        m_run[rb] = m_new;
+        tsum[rb] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) weights(rb, r);
       }
     }
   };
@@ -439,9 +439,7 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // fragment shared by the row blocks.  Element j of the V^T operand of k-step
   // ks is key 16*ks + (j < 4 ? 4*hh + j : 8 + 4*hh + j - 4): the first
   // transposing read covers j < 4, the second (8 rows further) j >= 4.
-  // `mid` runs between the first and the second half of the P.V MFMAs (the
-  // next tile's row maximum: VALU work for the matrix cores' shadow).
-  auto finish_pv = [&](const bf16x8 (&pf)[RB][2], const float (&tsum)[RB], int slot, auto mid) {
+  auto finish_pv = [&](const bf16x8 (&pf)[RB][2], const float (&tsum)[RB], int slot) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) l_run[rb] += tsum[rb];
     const char* Vs = smem + slot * L::STAGE_B + L::TILE_B;
@@ -462,7 +460,6 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
         for (int rb = 0; rb < RB; ++rb)
           oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[rb][ks], oacc[rb][db], 0, 0, 0);
       }
-      if (db == L::DB / 2 - 1) mid();
     }
     if (KG == 1) __builtin_amdgcn_s_setprio(0);
   };
@@ -498,8 +495,8 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // i+1 when DO_QK.  `slot` is an int or, in the loop unrolled by the ring
   // depth, a compile-time constant, so that the slot offsets fold into the
   // LDS reads' immediate offsets.
-  auto step = [&](auto do_qk_tag, auto tail_tag, auto next_tail_tag, int i, const Scores& s_in,
-                  Scores& s_out, auto slot) {
+  auto step = [&](auto do_qk_tag, auto tail_tag, int i, const Scores& s_in, Scores& s_out,
+                  auto slot) {
     constexpr bool DO_QK = decltype(do_qk_tag)::value;
     const int v_slot = slot;
     const int k_slot = (v_slot + 1) & (NS - 1);
@@ -513,9 +510,7 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     bf16x8 pf[RB][2];
     float tsum[RB];
     qk_softmax(do_qk_tag, tail_tag, s_in, t_begin + i, kf, Ks, pf, tsum, s_out);
-    finish_pv(pf, tsum, v_slot, [&] {
-      if constexpr (DO_QK && RB == 1) tile_max(next_tail_tag, s_out, t_begin + i + 1);
-    });
+    finish_pv(pf, tsum, v_slot);
   };
   const std::true_type yes{};
   const std::false_type no{};
@@ -539,12 +534,14 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) s_a[rb] = f32x16{};
   }
-  if constexpr (RB == 1) {
-    if ((t_begin + 1) * BN > n_keys)
-      tile_max(yes, s_a, t_begin);
-    else
-      tile_max(no, s_a, t_begin);
-  }
+  // The first tile's row maximum is the reference maximum (finite: the tile
+  // holds at least one key; a group without tiles takes its zero scores).
+  if ((t_begin + 1) * BN > n_keys)
+    tile_max(yes, s_a, t_begin);
+  else
+    tile_max(no, s_a, t_begin);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) m_run[rb] = mx_pend[rb];
   // Steady state, unrolled by two so that the score registers alternate
   // instead of being copied: both groups have tiles i and i+1 (group 0 has at
   // least nit - 1 tiles).
@@ -557,39 +554,34 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
     static_assert(NS == 4, "the steady-state slots below assume a 4-deep ring");
     for (; i + 7 < nit; i += 4) {
       advance_steady(i + 1, std::integral_constant<int, 3>{});
-      step(yes, no, no, i, s_a, s_b, std::integral_constant<int, 0>{});
+      step(yes, no, i, s_a, s_b, std::integral_constant<int, 0>{});
       advance_steady(i + 2, std::integral_constant<int, 0>{});
-      step(yes, no, no, i + 1, s_b, s_a, std::integral_constant<int, 1>{});
+      step(yes, no, i + 1, s_b, s_a, std::integral_constant<int, 1>{});
       advance_steady(i + 3, std::integral_constant<int, 1>{});
-      step(yes, no, no, i + 2, s_a, s_b, std::integral_constant<int, 2>{});
+      step(yes, no, i + 2, s_a, s_b, std::integral_constant<int, 2>{});
       advance_steady(i + 4, std::integral_constant<int, 2>{});
-      step(yes, no, no, i + 3, s_b, s_a, std::integral_constant<int, 3>{});
+      step(yes, no, i + 3, s_b, s_a, std::integral_constant<int, 3>{});
     }
   }
   for (; i + 3 < nit; i += 2) {
     advance(i + 1);
-    step(yes, no, no, i, s_a, s_b, slot_of(i));
+    step(yes, no, i, s_a, s_b, slot_of(i));
     advance(i + 2);
-    step(yes, no, no, i + 1, s_b, s_a, slot_of(i + 1));
+    step(yes, no, i + 1, s_b, s_a, slot_of(i + 1));
   }
   if (i + 2 < nit) {
     advance(i + 1);
-    step(yes, no, no, i, s_a, s_b, slot_of(i));
+    step(yes, no, i, s_a, s_b, slot_of(i));
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) s_a[rb] = s_b[rb];
     ++i;
   }
   if (nit >= 2) {   // tile nit-2; group 0 may lack tile nit-1
     advance(nit - 1);
-    if (nit - 1 < cnt) {
-      // The next tile, nit-1, is the sequence's last when it runs past the end.
-      if (RB == 1 && t_end * BN > n_keys)
-        step(yes, no, yes, nit - 2, s_a, s_b, slot_of(nit - 2));
-      else
-        step(yes, no, no, nit - 2, s_a, s_b, slot_of(nit - 2));
-    } else {
-      step(no, no, no, nit - 2, s_a, s_b, slot_of(nit - 2));
-    }
+    if (nit - 1 < cnt)
+      step(yes, no, nit - 2, s_a, s_b, slot_of(nit - 2));
+    else
+      step(no, no, nit - 2, s_a, s_b, slot_of(nit - 2));
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) s_a[rb] = s_b[rb];
   }
@@ -597,9 +589,9 @@ void attn_mfma_kernel(AttnParams p, int m_tiles, int n_blocks) {
   // always the group's tile nit-1.
   if (nit - 1 < cnt) {
     if (t_end * BN > n_keys)
-      step(no, yes, no, nit - 1, s_a, s_b, slot_of(nit - 1));
+      step(no, yes, nit - 1, s_a, s_b, slot_of(nit - 1));
     else
-      step(no, no, no, nit - 1, s_a, s_b, slot_of(nit - 1));
+      step(no, no, nit - 1, s_a, s_b, slot_of(nit - 1));
   }
 
   float l_tot[RB];
