@@ -185,6 +185,47 @@ def test_scale_variants_fp32(scale):
     check_attn(got, oracle_attn(inp), "fp32", False, f"fp32 scale={scale}")
 
 
+# Scores that rise by about 12 (base-2 units) per 32-key tile: every tile's
+# weights overflow the lazy bound against the reference the tile before left,
+# so the accumulators are rescaled at every tile; falling scores never rescale
+# after the first tile (later weights underflow towards zero).  Q ~ 1 + noise,
+# K_j ~ a_j + noise along the all-ones direction.
+def ramp_inputs(rising: bool, D: int, seed: int):
+    B, Hq, Hkv, P, L = 2, 8, 2, 200, 40
+    n = P + L
+    rng = np.random.default_rng(seed)
+    c = np.log2(np.e) / np.sqrt(D)
+    a = (12.0 / 32.0) / (D * c) * (np.arange(n) if rising else (n - 1 - np.arange(n)))
+    q = (1.0 + 0.25 * rng.standard_normal((B, Hq, L, D))).astype(np.float32)
+    k = (a[None, None, :, None] + 0.25 * rng.standard_normal((B, Hkv, n, D))).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, n, D)).astype(np.float32)
+    bits = synth.bf16_bits_from_f32
+    return dict(q=bits(q), k_ctx=bits(k[:, :, :P].copy()), v_ctx=bits(v[:, :, :P].copy()),
+                k_blk=bits(k[:, :, P:].copy()), v_blk=bits(v[:, :, P:].copy()), prefix_len=P,
+                prefix_cap=P, block_len=L, batch=B, scale=float(1.0 / np.sqrt(D)), dtype="bf16")
+
+
+@pytest.mark.parametrize("rising", [True, False])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("plan", [dict(path="mfma"), dict(path="mfma", kv_splits=3),
+                                  dict(path="mfma", kv_groups=2), dict(path="shuffle")],
+                         ids=["mfma", "mfma-splits3", "mfma-groups2", "shuffle"])
+def test_score_ramps_rescale(rising, D, plan):
+    inp = ramp_inputs(rising, D, seed=31)
+    got = gpu_attn(inp, DEV, out_dtype=torch.float32, **plan)
+    ref = oracle_attn(inp)
+    check_attn(got, ref, "bf16", False, f"ramp rising={rising} D={D} {plan}")
+    # The inputs do what the test is for: with rising scores every row's tile
+    # maximum clears the previous one by more than 8 at 6 of the 7 tile steps
+    # (the ragged last tile rises less); with falling scores at none.
+    q = as_f64(inp["q"])
+    k = np.repeat(np.concatenate([as_f64(inp["k_ctx"]), as_f64(inp["k_blk"])], axis=2), 4, axis=1)
+    s2 = np.einsum("bhld,bhnd->bhln", q, k) * np.log2(np.e) * inp["scale"]
+    tmax = np.stack([s2[..., t:t + 32].max(-1) for t in range(0, s2.shape[-1], 32)], -1)
+    jumps = (np.diff(tmax, axis=-1) > 8).sum(-1)
+    assert (jumps >= 6).all() if rising else (jumps == 0).all()
+
+
 def test_paths_agree_and_deterministic():
     cfg = small_cfg(batch=2, prefix_len=257, block_len=32)
     inp = synth.attn_inputs(cfg, seed=4)
