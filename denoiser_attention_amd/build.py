@@ -27,6 +27,13 @@ PROBE_LIB = os.path.join(PKG, "libtt_probes.so")
 # for the last build (read by the CPU tests that guard against spills).
 RESOURCES = os.path.join(BUILD, "kernel_resources.json")
 
+
+def device_asm(src: str) -> str:
+    """Path of the gfx950 assembly the last build wrote for a .hip source (read
+    by the CPU tests that check hazards the compiler cannot see through inline
+    asm)."""
+    return os.path.join(BUILD, os.path.basename(src) + ".s")
+
 SOURCES = ["tt_api.cpp", "attn_mfma.hip", "attn_shuffle.hip", "unmask.hip", "lmhead.hip"]
 PROBE_SOURCES = ["probes.hip"]
 ARCH = "gfx950"
@@ -80,6 +87,13 @@ def _compile(src: str, verbose: bool):
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(lines))
     resources = parse_resources("\n".join(lines))
+    if src.endswith(".hip"):
+        # The device assembly of the same source, for the hazard checks.
+        acmd = [hipcc(), *COMMON, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o",
+                device_asm(src)]
+        a = subprocess.run(acmd, capture_output=True, text=True)
+        if a.returncode != 0:
+            raise RuntimeError(f"hipcc -S failed on {src}:\n{a.stdout}{a.stderr}")
     # Everything but the resource remarks (and the source excerpts under them).
     msg = "\n".join(l for l in lines if "kernel-resource-usage" not in l and not re.match(r"^\s+(\d+ \||\|)", l))
     if msg.strip() and verbose:

@@ -156,6 +156,7 @@ hipError_t launch_topk_commit(const UnmaskParams& p, hipStream_t stream);
 constexpr int kLmRows = 256;     // hidden rows per workgroup
 constexpr int kLmVocab = 256;    // vocabulary entries per workgroup (one slice)
 constexpr int kLmK = 32;         // d_model granularity (stages take 64 columns, the last may take 32)
+constexpr int kLmWorkgroups = 256;   // persistent stats workgroups: one per CU of an MI355X
 struct LmParams {
   const void* hidden;        // [B*L, d] bf16
   const void* weight;        // [V, d] bf16

@@ -95,3 +95,69 @@ def test_parse_resources_on_sample():
     )
     assert B.parse_resources(text) == {
         "kern": {"vgprs": 74, "scratch_bytes": 8, "vgpr_spill": 3, "lds_bytes": 12424}}
+
+
+# --- Hazards the compiler cannot see through inline asm ---------------------
+#
+# The direct-to-LDS loads are written as inline asm.  On gfx950 a vector
+# instruction that writes a scalar register (v_readlane of a spilled scalar,
+# v_readfirstlane, a compare into an SGPR pair) needs 5 wait states before a
+# memory instruction reads that register; the compiler inserts them for the
+# instructions it generates, not for the operands of an asm statement.  A load
+# that reads its scalar base too early takes a stale address.  Every such load
+# in the built assembly must be at least 5 wait states (s_nop N counts N + 1)
+# after any vector write of its scalar operands, in program order.
+
+def _sgprs(tok):
+    m = re.match(r"s\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"s(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def dma_hazards(asm_text):
+    ins = []
+    for raw in asm_text.splitlines():
+        t = raw.strip()
+        if not t or t.startswith((";", ".")) or re.match(r"^[\w.$]+:", t):
+            continue
+        ins.append(t)
+    found = []
+    for k, t in enumerate(ins):
+        if not t.startswith("global_load_lds"):
+            continue
+        regs = set()
+        for tok in t.replace(",", " ").split()[1:]:
+            regs |= _sgprs(tok)
+        ws, b = 0, k - 1
+        while b >= 0 and ws < 5:
+            prev = ins[b]
+            if prev.startswith("v_"):
+                ops = prev.replace(",", " ").split()
+                if len(ops) > 1 and _sgprs(ops[1]) & regs:
+                    found.append((prev, ws, t))
+                    break
+            m = re.match(r"s_nop\s+(\d+)", prev)
+            ws += int(m.group(1)) + 1 if m else 1
+            b -= 1
+    return found
+
+
+def test_dma_hazard_check_catches_a_planted_case():
+    bad = "v_readlane_b32 s17, v246, 42\n\ts_mov_b32 m0, s5\n\tglobal_load_lds_dwordx4 v2, s[16:17]\n"
+    good = "v_readlane_b32 s17, v246, 42\n\ts_nop 4\n\tglobal_load_lds_dwordx4 v2, s[16:17]\n"
+    other = "v_readlane_b32 s20, v246, 42\n\tglobal_load_lds_dwordx4 v2, s[16:17]\n"
+    assert len(dma_hazards(bad)) == 1
+    assert dma_hazards(good) == [] and dma_hazards(other) == []
+
+
+def test_no_scalar_base_hazard_before_lds_dma():
+    _resources()   # the freshness check of the last build
+    for src in B.SOURCES + B.PROBE_SOURCES:
+        if not src.endswith(".hip"):
+            continue
+        path = B.device_asm(src)
+        assert os.path.exists(path), f"no device assembly for {src}: rebuild"
+        found = dma_hazards(open(path).read())
+        assert not found, f"{src}: {found[:3]}"
