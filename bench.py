@@ -389,8 +389,11 @@ def suite(args):
              for n in ("q", "k_ctx", "v_ctx", "k_blk", "v_blk")}
         lens = torch.from_numpy(inp["prefix_lens"]).to(dev)
         out = torch.empty_like(t["q"])
-        fn = lambda: tt.block_attn_varlen(t["q"], t["k_ctx"], t["v_ctx"], lens, 2048, t["k_blk"],
-                                          t["v_blk"], cfg.softmax_scale, out=out, stream=stream)
+        with torch.cuda.stream(stream):
+            fn = tt.prepare_block_attn_varlen(t["q"], t["k_ctx"], t["v_ctx"], lens, 2048,
+                                              t["k_blk"], t["v_blk"], cfg.softmax_scale, out,
+                                              stream=stream)
+        torch.cuda.synchronize()
         us = time_calls([fn])
         Ps = inp["prefix_lens"].astype(np.int64)
         B, Hq, Hkv, D, L = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_len
@@ -407,8 +410,10 @@ def suite(args):
             q, kn, vn = randn_bf16(1, Hq, T, D), randn_bf16(1, Hkv, T, D), randn_bf16(1, Hkv, T, D)
             kc, vc = randn_bf16(1, Hkv, T, D), randn_bf16(1, Hkv, T, D)
             out = torch.empty_like(q)
-            fn = lambda: tt.block_attn_multiblock(q, kc, vc, kn, vn, S, 1.0 / np.sqrt(D), out=out,
-                                                  stream=stream)
+            with torch.cuda.stream(stream):
+                fn = tt.prepare_block_attn_multiblock(q, kc, vc, kn, vn, S, 1.0 / np.sqrt(D), out,
+                                                      stream=stream)
+            torch.cuda.synchronize()
             us = time_calls([fn], n=max(5, reps // 4))
             keys = sum(j * S + S for j in range(nb))
             emit(f"attn multiblock {nb}x256 batch=1", us,

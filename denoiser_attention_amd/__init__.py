@@ -15,17 +15,19 @@ synthetic-input generator (``synth``).
 from ._binding import (  # noqa: F401
     LIB_PATH, SELECT_MODES, Prepared, Select, TTError, attn_multiblock_workspace_bytes,
     attn_workspace_bytes, block_attn, block_attn_multiblock, block_attn_varlen, lib,
-    lmhead_unmask_step, lmhead_unmask_workspace_bytes, prepare_lmhead_unmask_step,
-    prepare_block_attn, prepare_unmask_commit, prepare_unmask_commit_ex, prepare_unmask_reduce,
-    select_rule, status_string, unmask_commit, unmask_commit_ex, unmask_reduce, unmask_step,
-    unmask_step_ex, unmask_step_noalloc, unmask_workspace_bytes, version,
+    lmhead_unmask_step, lmhead_unmask_workspace_bytes, prepare_block_attn,
+    prepare_block_attn_multiblock, prepare_block_attn_varlen, prepare_lmhead_unmask_step,
+    prepare_unmask_commit, prepare_unmask_commit_ex, prepare_unmask_reduce, select_rule,
+    status_string, unmask_commit, unmask_commit_ex, unmask_reduce, unmask_step, unmask_step_ex,
+    unmask_step_noalloc, unmask_workspace_bytes, version,
 )
 
 __all__ = [
     "LIB_PATH", "SELECT_MODES", "Prepared", "Select", "TTError", "attn_multiblock_workspace_bytes",
-    "attn_workspace_bytes", "block_attn", "block_attn_multiblock", "block_attn_varlen",
-    "lmhead_unmask_step", "lmhead_unmask_workspace_bytes", "prepare_lmhead_unmask_step", "lib", "prepare_block_attn", "prepare_unmask_commit", "prepare_unmask_commit_ex",
-    "prepare_unmask_reduce", "select_rule", "status_string", "unmask_commit", "unmask_commit_ex",
-    "unmask_reduce", "unmask_step", "unmask_step_ex", "unmask_step_noalloc",
-    "unmask_workspace_bytes", "version",
+    "attn_workspace_bytes", "block_attn", "block_attn_multiblock", "block_attn_varlen", "lib",
+    "lmhead_unmask_step", "lmhead_unmask_workspace_bytes", "prepare_block_attn",
+    "prepare_block_attn_multiblock", "prepare_block_attn_varlen", "prepare_lmhead_unmask_step",
+    "prepare_unmask_commit", "prepare_unmask_commit_ex", "prepare_unmask_reduce", "select_rule",
+    "status_string", "unmask_commit", "unmask_commit_ex", "unmask_reduce", "unmask_step",
+    "unmask_step_ex", "unmask_step_noalloc", "unmask_workspace_bytes", "version",
 ]

@@ -237,6 +237,29 @@ def block_attn_varlen(q, k_ctx, v_ctx, prefix_lens, max_prefix_len, k_blk, v_blk
     """Eq. (1) with a prefix length per batch entry (tt_block_attn_varlen).
     ``prefix_lens`` is an int32 tensor [B] on the same GPU, every value in
     [0, max_prefix_len]."""
+    args, out, _ = _varlen_args(q, k_ctx, v_ctx, prefix_lens, max_prefix_len, k_blk, v_blk, scale,
+                                out, out_dtype, path, kv_splits, kv_groups, rows_per_wave,
+                                stream_waves, workspace, stream)
+    _check(lib().tt_block_attn_varlen(*args), "tt_block_attn_varlen")
+    return out
+
+
+def prepare_block_attn_varlen(q, k_ctx, v_ctx, prefix_lens, max_prefix_len, k_blk, v_blk, scale,
+                              out, *, path: str = "auto", kv_splits: int = 0, kv_groups: int = 0,
+                              rows_per_wave: int = 0, stream_waves: int = 0, workspace=None,
+                              stream=None):
+    """Validate once (same checks as block_attn_varlen), make one call, and
+    return a Prepared call."""
+    args, out, keep = _varlen_args(q, k_ctx, v_ctx, prefix_lens, max_prefix_len, k_blk, v_blk,
+                                   scale, out, None, path, kv_splits, kv_groups, rows_per_wave,
+                                   stream_waves, workspace, stream)
+    call = Prepared(lib().tt_block_attn_varlen, args, "tt_block_attn_varlen", keep)
+    call()
+    return call
+
+
+def _varlen_args(q, k_ctx, v_ctx, prefix_lens, max_prefix_len, k_blk, v_blk, scale, out, out_dtype,
+                 path, kv_splits, kv_groups, rows_per_wave, stream_waves, workspace, stream):
     _require(q.dim() == 4, "q must be [B, Hq, L, D]")
     device = q.device
     B, Hq, L, D = q.shape
@@ -263,13 +286,11 @@ def block_attn_varlen(q, k_ctx, v_ctx, prefix_lens, max_prefix_len, k_blk, v_blk
         with _on(stream):
             workspace = torch.empty(need, dtype=torch.uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().tt_block_attn_varlen(
-        _ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(prefix_lens), int(max_prefix_len), _ptr(k_blk),
-        _ptr(v_blk), L, Hq, Hkv, D, float(scale), _ptr(out), B, Pcap, _dtype_code(q.dtype),
-        _dtype_code(out.dtype), _ptr(workspace), ws_bytes, _stream(device, stream),
-        ctypes.byref(opts))
-    _check(st, "tt_block_attn_varlen")
-    return out
+    args = (_ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(prefix_lens), int(max_prefix_len), _ptr(k_blk),
+            _ptr(v_blk), L, Hq, Hkv, D, float(scale), _ptr(out), B, Pcap, _dtype_code(q.dtype),
+            _dtype_code(out.dtype), _ptr(workspace), ws_bytes, _stream(device, stream),
+            ctypes.byref(opts))
+    return args, out, (q, k_ctx, v_ctx, prefix_lens, k_blk, v_blk, out, workspace, opts)
 
 
 def attn_multiblock_workspace_bytes(batch, block_size, n_blocks, n_q_heads, n_kv_heads, head_dim,
@@ -292,6 +313,29 @@ def block_attn_multiblock(q, k_ctx, v_ctx, k_noisy, v_noisy, block_size, scale, 
     """Training-style pass over all noisy blocks (tt_block_attn_multiblock).
     q [B,Hq,N*S,D]; k_ctx/v_ctx [B,Hkv,cap,D] with cap >= (N-1)*S;
     k_noisy/v_noisy [B,Hkv,N*S,D]."""
+    args, out, _ = _multiblock_args(q, k_ctx, v_ctx, k_noisy, v_noisy, block_size, scale, out,
+                                    out_dtype, path, kv_splits, kv_groups, rows_per_wave,
+                                    stream_waves, workspace, stream)
+    _check(lib().tt_block_attn_multiblock(*args), "tt_block_attn_multiblock")
+    return out
+
+
+def prepare_block_attn_multiblock(q, k_ctx, v_ctx, k_noisy, v_noisy, block_size, scale, out, *,
+                                  path: str = "auto", kv_splits: int = 0, kv_groups: int = 0,
+                                  rows_per_wave: int = 0, stream_waves: int = 0, workspace=None,
+                                  stream=None):
+    """Validate once (same checks as block_attn_multiblock), make one call,
+    and return a Prepared call."""
+    args, out, keep = _multiblock_args(q, k_ctx, v_ctx, k_noisy, v_noisy, block_size, scale, out,
+                                       None, path, kv_splits, kv_groups, rows_per_wave,
+                                       stream_waves, workspace, stream)
+    call = Prepared(lib().tt_block_attn_multiblock, args, "tt_block_attn_multiblock", keep)
+    call()
+    return call
+
+
+def _multiblock_args(q, k_ctx, v_ctx, k_noisy, v_noisy, block_size, scale, out, out_dtype, path,
+                     kv_splits, kv_groups, rows_per_wave, stream_waves, workspace, stream):
     _require(q.dim() == 4, "q must be [B, Hq, N*S, D]")
     device = q.device
     B, Hq, T, D = q.shape
@@ -319,12 +363,10 @@ def block_attn_multiblock(q, k_ctx, v_ctx, k_noisy, v_noisy, block_size, scale, 
         with _on(stream):
             workspace = torch.empty(need, dtype=torch.uint8, device=device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().tt_block_attn_multiblock(
-        _ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(k_noisy), _ptr(v_noisy), S, N, Hq, Hkv, D,
-        float(scale), _ptr(out), B, cap, _dtype_code(q.dtype), _dtype_code(out.dtype),
-        _ptr(workspace), ws_bytes, _stream(device, stream), ctypes.byref(opts))
-    _check(st, "tt_block_attn_multiblock")
-    return out
+    args = (_ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(k_noisy), _ptr(v_noisy), S, N, Hq, Hkv, D,
+            float(scale), _ptr(out), B, cap, _dtype_code(q.dtype), _dtype_code(out.dtype),
+            _ptr(workspace), ws_bytes, _stream(device, stream), ctypes.byref(opts))
+    return args, out, (q, k_ctx, v_ctx, k_noisy, v_noisy, out, workspace, opts)
 
 
 def unmask_workspace_bytes(batch, block_len, vocab) -> int:

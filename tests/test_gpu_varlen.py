@@ -220,3 +220,41 @@ def test_multiblock_training_size_sampled():
     for (b, h), o in oracle_multiblock(inp, pairs=[(0, 0), (0, 17)]).items():
         check_attn(got[b, h], o, "bf16", True, f"multiblock 8x256 h={h}")
     assert np.isfinite(got).all()
+
+
+def test_prepared_calls_match():
+    """The prepared (validate once, reissue) varlen and multiblock calls the
+    benchmark times produce the unprepared calls' outputs bit for bit, on a
+    side stream, call after call."""
+    from denoiser_attention_amd import (block_attn_multiblock, block_attn_varlen,
+                                        prepare_block_attn_multiblock, prepare_block_attn_varlen)
+    st = torch.cuda.Stream(DEV)
+    cfg = base_cfg(batch=3, n_q_heads=8, n_kv_heads=2, prefix_len=300, block_len=21)
+    inp = synth.varlen_inputs(cfg, seed=41, max_prefix_len=300)
+    t = {n: to_dev(inp[n], DEV) for n in ("q", "k_ctx", "v_ctx", "k_blk", "v_blk")}
+    ld = torch.from_numpy(np.asarray(inp["prefix_lens"], dtype=np.int32)).to(DEV)
+    ref = block_attn_varlen(t["q"], t["k_ctx"], t["v_ctx"], ld, 300, t["k_blk"], t["v_blk"],
+                            inp["scale"], kv_splits=3)
+    out = torch.full_like(ref, 7.0)
+    with torch.cuda.stream(st):
+        call = prepare_block_attn_varlen(t["q"], t["k_ctx"], t["v_ctx"], ld, 300, t["k_blk"],
+                                         t["v_blk"], inp["scale"], out, kv_splits=3, stream=st)
+        for _ in range(3):
+            call()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+    S, N = 16, 3
+    mb = synth.multiblock_inputs(base_cfg(batch=2, n_q_heads=4, n_kv_heads=2), n_blocks=N,
+                                 block_size=S, seed=42)
+    m = {n: to_dev(mb[n], DEV) for n in ("q", "k_ctx", "v_ctx", "k_noisy", "v_noisy")}
+    ref = block_attn_multiblock(m["q"], m["k_ctx"], m["v_ctx"], m["k_noisy"], m["v_noisy"], S,
+                                mb["scale"])
+    out = torch.full_like(ref, 7.0)
+    with torch.cuda.stream(st):
+        call = prepare_block_attn_multiblock(m["q"], m["k_ctx"], m["v_ctx"], m["k_noisy"],
+                                             m["v_noisy"], S, mb["scale"], out, stream=st)
+        for _ in range(3):
+            call()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
