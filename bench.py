@@ -23,8 +23,10 @@ of load to ramp up, so the timed steps see steady clocks whatever W is.
 Prints ONE JSON line: block-tokens/s over the timed steps; the roofline of
 the dominant kernel of the step (the one with the longest average launch,
 timed by HIP events around a back-to-back loop of that kernel alone on the
-launch stream); both kernels' figures; and the CPU oracle timed on a bounded
-sample of the same workload on the host cores.
+launch stream); both kernels' figures; the CPU oracle timed on a bounded
+sample of the same workload on the host cores; and (default workload only,
+--no-side skips them) the attention calls of the other configurations and
+the step of the 256-token block, each with its fraction of the roof.
 """
 from __future__ import annotations
 
@@ -58,6 +60,8 @@ def parse_args():
     ap.add_argument("--prefix-len", type=int, default=None)
     ap.add_argument("--rotate", type=int, default=0, help="input sets rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side", action="store_true",
+                    help="skip the other configurations' attention calls and 256-token step")
     ap.add_argument("--graph", action="store_true",
                     help="replay one captured HIP graph per input set instead of eager calls")
     ap.add_argument("--suite", action="store_true",
@@ -203,6 +207,117 @@ def _roof(bytes_, flops):
     return max(t_hbm, t_mfma), ("hbm" if t_hbm >= t_mfma else "mfma")
 
 
+def time_calls_on(torch, stream, fns, n):
+    """Average us per call over n back-to-back calls (rotating fns), HIP events
+    on the launch stream, after at least 50 ms of untimed calls (the clocks
+    ramp up under load)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < 0.05:
+            for _ in range(8):
+                fns[i % len(fns)]()
+                i += 1
+            stream.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fns[i % len(fns)]()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / n
+
+
+def rotated_sets(set_bytes, cap=48):
+    """Independent input sets whose one pass exceeds 1 GB (four times the
+    Infinity Cache), so that every call streams its inputs from HBM."""
+    return int(min(cap, max(2, np.ceil(1.0e9 / set_bytes))))
+
+
+def attn_bytes_flops(B, Hq, Hkv, D, L, P, s=2):
+    """Algorithmic bytes and flops of one attention call."""
+    return (s * (2 * B * Hq * L * D + 2 * B * Hkv * (P + L) * D), 4 * B * Hq * L * (P + L) * D)
+
+
+def attention_calls(torch, tt, dev, stream, B, Hq, Hkv, D, L, P, scale, path="auto", n_sets=None):
+    """Prepared attention calls over rotated N(0,1) bf16 input sets drawn on the
+    device; returns (calls, buffers to keep alive)."""
+    n_sets = n_sets or rotated_sets(attn_bytes_flops(B, Hq, Hkv, D, L, P)[0])
+
+    def rnd(*shape):
+        return torch.randn(*shape, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    fns, keep = [], []
+    for _ in range(n_sets):
+        t = dict(q=rnd(B, Hq, L, D), k_ctx=rnd(B, Hkv, P, D), v_ctx=rnd(B, Hkv, P, D),
+                 k_blk=rnd(B, Hkv, L, D), v_blk=rnd(B, Hkv, L, D))
+        out = torch.empty_like(t["q"])
+        with torch.cuda.stream(stream):
+            fns.append(tt.prepare_block_attn(t["q"], t["k_ctx"], t["v_ctx"], P, t["k_blk"],
+                                             t["v_blk"], scale, out, path=path, stream=stream))
+        keep.append((t, out))
+    torch.cuda.synchronize()
+    return fns, keep
+
+
+# Attention calls of the other configurations, timed in the default run.
+SIDE_ATTENTION = (("decode_b8_p2048_l32", {}), ("block256_b16_p1024", {}),
+                  ("gen8k_b4_l256", {"prefix_len": 16128}), ("decode_l16", {}), ("decode_l1", {}))
+
+
+def side_workloads(torch, tt, synth, dev, stream, logits_sets, reps=40):
+    """The other configurations' attention calls, and the step of the 256-token
+    block (its attention plus the unmask of its 4096 positions, read from the
+    same 4096 logit rows as the default workload's), so that the default run
+    records every workload's roof fraction.  The --suite lines cover them in
+    more depth (every step of a block, the measured roofs)."""
+    lines, block = [], None
+    for name, kw in SIDE_ATTENTION:
+        c = synth.get_config(name, **kw)
+        B, Hq, Hkv, D, L, P = (c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.block_len,
+                               c.prefix_len)
+        bytes_, flops = attn_bytes_flops(B, Hq, Hkv, D, L, P)
+        fns, keep = attention_calls(torch, tt, dev, stream, B, Hq, Hkv, D, L, P, c.softmax_scale,
+                                    n_sets=rotated_sets(bytes_, cap=16))
+        us = time_calls_on(torch, stream, fns, reps)
+        roof_s, bound = _roof(bytes_, flops)
+        lines.append({"workload": name + (f" P={P}" if kw else ""), "op": "attention",
+                      "avg_call_us": us, "bound": bound, "roof_us": roof_s * 1e6,
+                      "roof_frac": roof_s * 1e6 / us, "TFLOPs": flops / us / 1e6,
+                      "GBps": bytes_ / us / 1e3})
+        if name == "block256_b16_p1024":
+            block = (c, fns, keep, us)
+        else:
+            del fns, keep
+    c, fns, keep, attn_us = block
+    B, L, V = c.batch, c.block_len, c.vocab
+    assert all(x.numel() == B * L * V for x in logits_sets)
+    mask = torch.ones((B, L), dtype=torch.uint8, device=dev)
+    mask_out = torch.empty_like(mask)
+    tokens = torch.full((B, L), -1, dtype=torch.int32, device=dev)
+    ws = torch.empty(tt.unmask_workspace_bytes(B, L, V), dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(stream):
+        reds = [tt.prepare_unmask_reduce(x.view(B, L, V), mask, ws, stream=stream)
+                for x in logits_sets]
+        com = tt.prepare_unmask_commit(mask, c.k, tokens, mask_out, V, ws, stream=stream)
+    torch.cuda.synchronize()
+    n = max(len(fns), len(reds))
+    steps = []
+    for j in range(n):
+        def one(a=fns[j % len(fns)], r=reds[j % len(reds)]):
+            a()
+            r()
+            com()
+        steps.append(one)
+    us = time_calls_on(torch, stream, steps, reps)
+    lines.append({"workload": c.name, "op": "step (attention + unmask of all 4096 positions, k=32)",
+                  "avg_step_us": us, "block_tokens_per_s": B * L / (us * 1e-6),
+                  "attention_us": attn_us})
+    del fns, keep, reds
+    return lines
+
+
 SUITE_SECTIONS = ("probes", "attention", "gen8k_sweep", "varlen", "multiblock", "unmask",
                   "selection", "trace8k", "layers6", "crossover", "lmhead")
 
@@ -243,25 +358,7 @@ def suite(args):
     measured = {}    # measured roofs: "hbm" GB/s, "mfma" TFLOP/s
 
     def time_calls(fns, n=reps):
-        """Average us per call over back-to-back calls (rotating fns), HIP events
-        on the launch stream, after at least 50 ms of untimed calls (the clocks
-        ramp up under load)."""
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            t0 = time.perf_counter()
-            i = 0
-            while time.perf_counter() - t0 < 0.05:
-                for _ in range(8):
-                    fns[i % len(fns)]()
-                    i += 1
-                stream.synchronize()
-            e0.record(stream)
-            for i in range(n):
-                fns[i % len(fns)]()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        return 1e3 * e0.elapsed_time(e1) / n
+        return time_calls_on(torch, stream, fns, n)
 
     def fracs(us, bytes_, flops):
         roof_s, bound = _roof(bytes_, flops)
@@ -279,32 +376,17 @@ def suite(args):
         line.update(extra)
         print(json.dumps(line), flush=True)
 
-    def n_rotate(set_bytes, cap=48):
-        # Enough independent input sets that one pass over them exceeds 1 GB
-        # (four times the Infinity Cache).
-        return int(min(cap, max(2, np.ceil(1.0e9 / set_bytes))))
+    n_rotate = rotated_sets
 
     def randn_bf16(*shape):
         return torch.randn(*shape, device=dev, dtype=torch.float32).to(torch.bfloat16)
-
-    def attn_bytes_flops(B, Hq, Hkv, D, L, P, s=2):
-        return (s * (2 * B * Hq * L * D + 2 * B * Hkv * (P + L) * D), 4 * B * Hq * L * (P + L) * D)
 
     def attn_case(name, B, Hq, Hkv, D, L, P, scale=None, path="auto", extra=None, n=None):
         scale = 1.0 / np.sqrt(D) if scale is None else scale
         bytes_, flops = attn_bytes_flops(B, Hq, Hkv, D, L, P)
         n_sets = n_rotate(bytes_)
-        fns, keep = [], []
-        for _ in range(n_sets):
-            t = dict(q=randn_bf16(B, Hq, L, D), k_ctx=randn_bf16(B, Hkv, P, D),
-                     v_ctx=randn_bf16(B, Hkv, P, D), k_blk=randn_bf16(B, Hkv, L, D),
-                     v_blk=randn_bf16(B, Hkv, L, D))
-            out = torch.empty_like(t["q"])
-            with torch.cuda.stream(stream):
-                fns.append(tt.prepare_block_attn(t["q"], t["k_ctx"], t["v_ctx"], P, t["k_blk"],
-                                                 t["v_blk"], scale, out, path=path, stream=stream))
-            keep.append((t, out))
-        torch.cuda.synchronize()
+        fns, keep = attention_calls(torch, tt, dev, stream, B, Hq, Hkv, D, L, P, scale, path,
+                                    n_sets)
         us = time_calls(fns, n=n or reps)
         ex = dict(kind="attention", B=B, P=P, L=L, Hq=Hq, Hkv=Hkv, D=D, path=path,
                   workspace_bytes=tt.attn_workspace_bytes(B, P, L, Hq, Hkv, D, torch.bfloat16,
@@ -869,6 +951,10 @@ def main():
             "avg_launch_us": attn_us, "timing": timing,
         }
 
+    side = None
+    if not args.no_side and cfg.name == DEFAULT_CONFIG:
+        side = side_workloads(torch, tt, synth, dev, stream, [t["logits"] for t in sets])
+
     result = {
         "metric": METRIC,
         "value": B * L / (ms_step * 1e-3),
@@ -901,6 +987,7 @@ def main():
         "step_launch": "HIP graph replay per step" if graphs is not None else "eager calls",
         "graph_check": graph_check,
         "cpu_baseline": cpu,
+        "other_workloads": side,
     }
     print(json.dumps(result), flush=True)
 

@@ -26,7 +26,7 @@ def test_help_lists_every_mode():
     assert r.returncode == 0
     for flag in ("--gpus", "--steps", "--warmup", "--config", "--suite", "--attn-only",
                  "--lmhead-only", "--kernel-reps", "--copy-calibration", "--no-cpu-baseline",
-                 "--graph"):
+                 "--graph", "--no-side"):
         assert flag in r.stdout, flag
 
 
