@@ -102,12 +102,24 @@ def copy_calibration():
 KERNEL_SOURCES = {"vocab_reduce": "unmask.hip", "attn_mfma": "attn_mfma.hip"}
 
 
+def code_digest(text: str) -> str:
+    """Digest of C++/HIP source code with its // comments, indentation and
+    blank lines removed: a change of wording in a comment keeps it, any change
+    of code changes it."""
+    lines = []
+    for line in text.splitlines():
+        code = line.split("//", 1)[0].strip()
+        if code:
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
+
+
 def kernel_source_digest(kernel: str = "vocab_reduce") -> str:
-    """Digest of a kernel's source file; counter-derived traffic is only
+    """Code digest of a kernel's source file; counter-derived traffic is only
     reported while it matches the digest recorded with the counters."""
     path = os.path.join(ROOT, "denoiser_attention_amd", "csrc", KERNEL_SOURCES[kernel])
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    with open(path, encoding="utf-8") as fh:
+        return code_digest(fh.read())
 
 
 def recorded_traffic(workload: str, kernel: str = "vocab_reduce"):
@@ -120,7 +132,7 @@ def recorded_traffic(workload: str, kernel: str = "vocab_reduce"):
         return None
     text = open(path).read()
     m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    d = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    d = re.search(r"kernel_code_sha256_16:\s*([0-9a-f]+)", text)
     if not m or not d or d.group(1) != kernel_source_digest(kernel):
         return None
     return float(m.group(1))

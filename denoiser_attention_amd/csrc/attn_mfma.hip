@@ -14,7 +14,8 @@
 //     them: every K/V byte fetched from HBM feeds G*L query rows.
 //   * K/V stream: 32-key tiles go straight from global memory into a ring of
 //     NS LDS stages with 16-byte direct-to-LDS loads (no register staging, no
-//     LDS store instructions); NS-1 tiles are in flight while one is consumed.
+//     LDS store instructions); while one tile's V and the next tile's K are
+//     read, NS-2 further tiles stream in.
 //     Waits are explicit vmcnt counts and raw barriers, so that loads of later
 //     stages stay in flight across the barrier.
 //   * LDS layout: K and V tiles are row-major with the 16-byte chunks of each

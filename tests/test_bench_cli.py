@@ -47,3 +47,19 @@ def test_cpu_baseline_sample_on_host():
     assert res["value"] > 0 and res["cores"] >= 1
     assert res["cores_per_leg"]["unmask_processes"] == res["cores"]
     assert "scaled x1.5" in res["sample"]
+
+
+def test_code_digest_ignores_comments_only():
+    """The digest that ties counter-derived traffic to a kernel's source keeps
+    its value across comment and layout edits and changes with any code."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    a = "int f(int x) {  // twice\n  return 2 * x;\n}\n"
+    b = "// doubles\nint f(int x) {    // two times x\n\n    return 2 * x;\n}\n"
+    c = "int f(int x) {  // twice\n  return 3 * x;\n}\n"
+    assert bench.code_digest(a) == bench.code_digest(b)
+    assert bench.code_digest(a) != bench.code_digest(c)
+    for kernel in bench.KERNEL_SOURCES:
+        assert len(bench.kernel_source_digest(kernel)) == 16
+
