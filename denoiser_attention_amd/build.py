@@ -112,8 +112,40 @@ def _link(objs, out, verbose):
     os.replace(tmp, out)
 
 
+# A plain C99 client of the C ABI (include/tt.h + the HIP runtime, no Python),
+# built next to its source and run by the tests.
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c", "tt_c_client.c")
+C_CLIENT = os.path.join(ROOT, "tests", "c", "tt_c_client")
+
+
+def c_client_command(src: str, out: str) -> list:
+    """gcc command that builds a C99 program against include/tt.h and libtt.so
+    (found at run time next to the program's relative path to the package)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler found for the C ABI client")
+    rel = os.path.relpath(PKG, os.path.dirname(os.path.abspath(out)))
+    return [cc, "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+            "-I", INCLUDE, "-I", os.path.join(rocm, "include"), src, "-o", out,
+            "-L", PKG, "-ltt", f"-Wl,-rpath,$ORIGIN/{rel}",
+            "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+
+
+def _build_c_client(verbose):
+    tmp = C_CLIENT + ".tmp"
+    cmd = c_client_command(C_CLIENT_SRC, tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C client build failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, C_CLIENT)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libtt.so and libtt_probes.so.  Always rebuilds."""
+    """Compile every source and link libtt.so and libtt_probes.so, then the C
+    client of the ABI.  Always rebuilds."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = SOURCES + PROBE_SOURCES
     with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
@@ -124,6 +156,7 @@ def build(verbose: bool = False) -> str:
         json.dump(resources, f, indent=1, sort_keys=True)
     _link([objs[s] for s in SOURCES], LIB, verbose)
     _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
+    _build_c_client(verbose)
     return LIB
 
 
