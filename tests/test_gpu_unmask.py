@@ -193,3 +193,22 @@ def test_deterministic():
     b = gpu_unmask(x, mask, 16, tokens, DEV)
     for key in a:
         assert np.array_equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("shift", [1, 2, 3])
+def test_logits_base_not_16_byte_aligned(shift):
+    """Logits that start 4, 8 or 12 bytes past a 16-byte boundary (a
+    contiguous view into a larger buffer), with V a multiple of 4: the rows are
+    not 16-byte aligned, so the vocabulary pass takes its scalar-load form and
+    still gives the oracle's ids, confidences and commits."""
+    B, L, V, k = 2, 12, 8192 + 4, 3
+    rng = np.random.default_rng(90 + shift)
+    x = (rng.standard_normal((B, L, V)) * 3).astype(np.float32)
+    mask = (rng.random((B, L)) < 0.75).astype(np.uint8)
+    buf = torch.empty(B * L * V + shift, dtype=torch.float32, device=DEV)
+    view = buf[shift:].view(B, L, V)
+    assert view.data_ptr() % 16 == 4 * shift
+    view.copy_(torch.from_numpy(x))
+    tokens = np.full((B, L), MASK_ID, np.int32)
+    got = gpu_unmask(view, mask, k, tokens, DEV)
+    check_unmask(got, oracle.unmask_step(x, mask, k), mask, k, tokens, f"base+{4 * shift}B")
