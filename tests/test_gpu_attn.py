@@ -296,14 +296,18 @@ def test_full_size_sampled(name, kw, batches, heads):
 
 
 # Sizes past the configurations: a 262K-key context (8193 key tiles, 268 MB of
-# cache K/V for one sequence), a 512-pair single-token batch, and a 64K-key
-# fp32 context on the shuffle kernel.
+# cache K/V for one sequence), a 512-pair single-token batch, a 64K-key fp32
+# context on the shuffle kernel, and one 4095-token bidirectional block.
 LARGE = [
     ("decode_b8_p2048_l32", dict(batch=1, prefix_len=262133, prefix_cap=262144, block_len=16),
      [0], [0, 31], "bf16"),
     ("decode_b8_p2048_l32", dict(batch=256, prefix_len=1000, block_len=1), [0, 255], [0, 31],
      "bf16"),
     ("tiny_fp32", dict(prefix_len=65531, prefix_cap=65536), [0], [0, 3], "fp32"),
+    # one long bidirectional block with no prefix: 65536 packed rows per KV head
+    # (512 query tiles each), 4095 keys (a ragged last key tile)
+    ("decode_b8_p2048_l32", dict(batch=1, prefix_len=0, prefix_cap=0, block_len=4095), [0],
+     [0, 17, 31], "bf16"),
 ]
 
 
